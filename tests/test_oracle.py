@@ -1,0 +1,274 @@
+"""Pins for the CPU oracle: brute force, closed forms, invariants, a library
+routine and the pages' overflow example. None of them re-types the oracle's
+own vectorised formula.
+
+Each pin is a function of an attention implementation ``fn(q, k, v, scale,
+causal) -> (O, lse)`` so that the same pins can be run against planted
+mistakes (``test_pins_catch_planted_mistakes``): every mutant below must fail
+at least one pin.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention_bruteforce, attention_fp64, attention_rows_fp64, head_forward
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
+
+
+def rand(shape, seed, amp=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * amp
+
+
+# ---------------------------------------------------------------- pins ----
+
+def pin_bruteforce(fn):
+    """Tiny shapes against pure-Python loops (math.exp / math.fsum)."""
+    for (B, H, Sq, Sk, D, causal, seed) in [
+        (1, 1, 1, 1, 1, False, 1), (2, 1, 3, 5, 2, False, 2), (1, 2, 5, 3, 4, True, 3),
+        (2, 2, 7, 7, 3, True, 4), (1, 1, 2, 7, 4, True, 5), (1, 2, 7, 2, 2, False, 6),
+    ]:
+        q = rand((B, H, Sq, D), seed)
+        k = rand((B, H, Sk, D), seed + 100)
+        v = rand((B, H, Sk, D), seed + 200)
+        scale = 0.7
+        o, lse = fn(q, k, v, scale, causal)
+        ob, lb = attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), scale, causal)
+        assert np.max(np.abs(o - ob)) <= 1e-12
+        assert np.max(np.abs(lse - lb)) <= 1e-12
+
+
+def pin_constant_v(fn):
+    """v_j = c for all j  =>  O_i = c for every mask."""
+    q = rand((1, 2, 9, 8), 11)
+    k = rand((1, 2, 9, 8), 12)
+    c = rand((8,), 13)
+    v = np.broadcast_to(c, (1, 2, 9, 8)).copy()
+    for causal in (False, True):
+        o, _ = fn(q, k, v, 0.35, causal)
+        assert np.max(np.abs(o - c)) <= 1e-13
+
+
+def pin_zero_q(fn):
+    """Q = 0: non-causal O_i = mean_j v_j, lse = ln Sk; causal prefix means, lse = ln(i+1)."""
+    Sq, Sk, D = 6, 6, 4
+    q = np.zeros((1, 1, Sq, D))
+    k = rand((1, 1, Sk, D), 21)
+    v = rand((1, 1, Sk, D), 22)
+    o, lse = fn(q, k, v, 1.3, False)
+    assert np.allclose(o[0, 0], v[0, 0].mean(axis=0)[None, :], atol=1e-14, rtol=0)
+    assert np.allclose(lse[0, 0], math.log(Sk), atol=1e-14, rtol=0)
+    o, lse = fn(q, k, v, 1.3, True)
+    for i in range(Sq):
+        assert np.allclose(o[0, 0, i], v[0, 0, : i + 1].mean(axis=0), atol=1e-14, rtol=0)
+        assert abs(lse[0, 0, i] - math.log(i + 1)) <= 1e-14
+
+
+def pin_causal_row0(fn):
+    """Causal row 0 sees only key 0: O_0 = v_0, lse_0 = scale * q_0 . k_0."""
+    q = rand((2, 1, 5, 6), 31)
+    k = rand((2, 1, 5, 6), 32)
+    v = rand((2, 1, 5, 6), 33)
+    o, lse = fn(q, k, v, 0.9, True)
+    for b in range(2):
+        assert np.max(np.abs(o[b, 0, 0] - v[b, 0, 0])) <= 1e-14
+        dot = math.fsum(q[b, 0, 0, d] * k[b, 0, 0, d] for d in range(6))
+        assert abs(lse[b, 0, 0] - 0.9 * dot) <= 1e-13
+
+
+def pin_single_key(fn):
+    """Sk = 1: O = v_0 for every row; lse = scale * q . k_0."""
+    q = rand((1, 1, 4, 5), 41)
+    k = rand((1, 1, 1, 5), 42)
+    v = rand((1, 1, 1, 5), 43)
+    o, lse = fn(q, k, v, 0.5, False)
+    assert np.max(np.abs(o[0, 0] - v[0, 0, 0])) <= 1e-14
+    for i in range(4):
+        dot = math.fsum(q[0, 0, i, d] * k[0, 0, 0, d] for d in range(5))
+        assert abs(lse[0, 0, i] - 0.5 * dot) <= 1e-13
+
+
+def pin_two_keys(fn):
+    """Two keys: O = sigma(s0-s1) v0 + sigma(s1-s0) v1, lse = ln(e^s0 + e^s1)."""
+    q = rand((1, 1, 3, 4), 51)
+    k = rand((1, 1, 2, 4), 52)
+    v = rand((1, 1, 2, 4), 53)
+    scale = 0.8
+    o, lse = fn(q, k, v, scale, False)
+    for i in range(3):
+        s = [scale * math.fsum(q[0, 0, i, d] * k[0, 0, j, d] for d in range(4)) for j in range(2)]
+        w0 = 1.0 / (1.0 + math.exp(s[1] - s[0]))
+        w1 = 1.0 / (1.0 + math.exp(s[0] - s[1]))
+        want = w0 * v[0, 0, 0] + w1 * v[0, 0, 1]
+        assert np.max(np.abs(o[0, 0, i] - want)) <= 1e-14
+        hi = max(s)
+        assert abs(lse[0, 0, i] - (hi + math.log1p(math.exp(min(s) - hi)))) <= 1e-14
+
+
+def pin_linear_in_v(fn):
+    """O is linear in V (P does not depend on V)."""
+    q = rand((1, 2, 7, 4), 61)
+    k = rand((1, 2, 9, 4), 62)
+    v1 = rand((1, 2, 9, 4), 63)
+    v2 = rand((1, 2, 9, 4), 64)
+    for causal in (False, True):
+        a, _ = fn(q, k, v1, 0.6, causal)
+        b, _ = fn(q, k, v2, 0.6, causal)
+        c, _ = fn(q, k, v1 - 2.5 * v2, 0.6, causal)
+        assert np.max(np.abs(c - (a - 2.5 * b))) <= 1e-12
+
+
+def pin_key_permutation(fn):
+    """Non-causal: permuting the rows of K and V together changes nothing."""
+    q = rand((1, 1, 5, 4), 71)
+    k = rand((1, 1, 8, 4), 72)
+    v = rand((1, 1, 8, 4), 73)
+    perm = np.random.default_rng(74).permutation(8)
+    a, la = fn(q, k, v, 0.9, False)
+    b, lb = fn(q, k[:, :, perm], v[:, :, perm], 0.9, False)
+    assert np.max(np.abs(a - b)) <= 1e-13 and np.max(np.abs(la - lb)) <= 1e-13
+
+
+def pin_library_sdpa(fn):
+    """torch's scaled_dot_product_attention (math path, fp64, CPU), top-left causal;
+    lse from torch.logsumexp over the masked, scaled scores."""
+    for (Sq, Sk, causal, seed) in [(33, 33, False, 81), (40, 40, True, 82), (17, 29, True, 83),
+                                   (29, 17, True, 84), (20, 50, False, 85)]:
+        q = rand((2, 3, Sq, 16), seed)
+        k = rand((2, 3, Sk, 16), seed + 1)
+        v = rand((2, 3, Sk, 16), seed + 2)
+        scale = 0.25
+        o, lse = fn(q, k, v, scale, causal)
+        tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            tq, tk, tv, is_causal=causal, scale=scale).numpy()
+        assert np.max(np.abs(o - ref)) <= 1e-10
+        s = torch.matmul(tq, tk.transpose(-1, -2).contiguous()) * scale
+        if causal:
+            s = s.masked_fill(torch.ones(Sq, Sk, dtype=torch.bool).triu(1), float("-inf"))
+        assert np.max(np.abs(lse - torch.logsumexp(s, dim=-1).numpy())) <= 1e-10
+
+
+def pin_large_logits(fn):
+    """Logits far past the fp16 exp-overflow point stay finite (safe softmax).
+
+    The pages put that point at a scaled logit of ln(65504) ~ 11.09, a raw
+    logit of ~88.7 at head_dim 64. Here one key leads by ~1000: O = v_lead,
+    lse = the leading score.
+    """
+    facts = json.load(open(GOLDEN))["fp16_exp_overflow"]
+    assert abs(math.log(facts["fp16_max"]) - facts["ln_fp16_max"]) < 5e-3
+    assert abs(facts["ln_fp16_max"] * math.sqrt(facts["head_dim"]) - facts["raw_logit_threshold"]) < 0.05
+    D = facts["head_dim"]
+    scale = 1.0 / math.sqrt(D)
+    q = np.zeros((1, 1, 2, D))
+    k = np.zeros((1, 1, 3, D))
+    q[0, 0, :, 0] = 100.0
+    k[0, 0, 0, 0] = 80.0    # score 1000
+    k[0, 0, 1, 0] = -20.0   # score -250
+    k[0, 0, 2, 0] = 10.0    # score 125 (>> 11.09: would overflow a naive fp16 exp)
+    v = rand((1, 1, 3, D), 91)
+    o, lse = fn(q, k, v, scale, False)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    assert np.max(np.abs(o[0, 0] - v[0, 0, 0])) <= 1e-14
+    assert np.max(np.abs(lse[0, 0] - 1000.0)) <= 1e-12
+
+
+PINS = [pin_bruteforce, pin_constant_v, pin_zero_q, pin_causal_row0, pin_single_key,
+        pin_two_keys, pin_linear_in_v, pin_key_permutation, pin_library_sdpa,
+        pin_large_logits]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(attention_fp64)
+
+
+def test_softmax_rows():
+    """P >= 0, rows sum to 1, masked entries are exactly 0."""
+    q = rand((7, 6), 101)
+    k = rand((11, 6), 102)
+    v = rand((11, 6), 103)
+    for causal in (False, True):
+        _, _, p = head_forward(q, k, v, 0.4, causal, return_p=True)
+        assert np.all(p >= 0)
+        assert np.max(np.abs(p.sum(axis=1) - 1.0)) <= 1e-12
+        if causal:
+            assert np.all(p[np.triu_indices(7, 1, 11)] == 0.0)
+
+
+def test_rows_match_full():
+    q = rand((2, 2, 40, 8), 111)
+    k = rand((2, 2, 40, 8), 112)
+    v = rand((2, 2, 40, 8), 113)
+    for causal in (False, True):
+        o, lse = attention_fp64(q, k, v, 0.3, causal)
+        rows = [0, 5, 17, 39]
+        orow, lrow = attention_rows_fp64(q, k, v, 0.3, causal, 1, 0, rows)
+        assert np.array_equal(orow, o[1, 0, rows]) and np.array_equal(lrow, lse[1, 0, rows])
+
+
+# ------------------------------------------------- planted mistakes ------
+
+def _mutant(kind):
+    def fn(q, k, v, scale, causal):
+        B, H, Sq, D = q.shape
+        Sk = k.shape[2]
+        o = np.empty((B, H, Sq, D))
+        lse = np.empty((B, H, Sq))
+        for b in range(B):
+            for h in range(H):
+                qq, kk, vv = q[b, h], k[b, h], v[b, h]
+                s = qq @ kk.T * (1.0 if kind == "no_scale" else scale)
+                if causal:
+                    i = np.arange(Sq)[:, None]
+                    j = np.arange(Sk)[None, :]
+                    bad = {"mask_diag": j >= i, "mask_flip": j < i}.get(kind, j > i)
+                    s = np.where(bad, -np.inf, s)
+                m = s.max(axis=1, keepdims=True)
+                if kind == "no_max":
+                    m = np.zeros_like(m)
+                with np.errstate(all="ignore"):
+                    p = np.exp(s - m)
+                    l = p.sum(axis=1, keepdims=True)
+                    pn = p if kind == "no_norm" else p / l
+                    if kind == "col_softmax":
+                        pn = p / p.sum(axis=0, keepdims=True)
+                    o[b, h] = pn @ (kk if kind == "uses_k" else vv)
+                    if kind == "lse_no_m":
+                        lse[b, h] = np.log(l[:, 0])
+                    elif kind == "lse_log2":
+                        lse[b, h] = m[:, 0] + np.log2(l[:, 0])
+                    else:
+                        lse[b, h] = m[:, 0] + np.log(l[:, 0])
+        return o, lse
+    return fn
+
+
+MUTANTS = ["no_scale", "mask_diag", "mask_flip", "no_max", "no_norm", "col_softmax",
+           "uses_k", "lse_no_m", "lse_log2"]
+
+
+@pytest.mark.parametrize("kind", MUTANTS)
+def test_pins_catch_planted_mistakes(kind):
+    fn = _mutant(kind)
+    failed = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(fn)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {kind!r}"
+
+
+def test_pins_accept_correct_copy():
+    """The mutant scaffold without a mistake passes every pin (so the pins
+    fail mutants for the planted mistake, not for the scaffold)."""
+    fn = _mutant("none")
+    for pin in PINS:
+        pin(fn)
