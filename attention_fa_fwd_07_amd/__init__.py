@@ -1,0 +1,144 @@
+"""Python binding of libfa_mi355x (FlashAttention forward, MI355X / gfx950).
+
+Argument marshalling only: every step of the attention forward runs in the
+HIP kernels of ``libfa_mi355x.so``. torch supplies device memory and the
+current stream. There is no fallback: if the library is missing or the
+tensors are not on a GPU, the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa_mi355x.so")
+
+# status codes (include/fa_mi355x.h)
+FA_OK = 0
+FA_ERR_NULL_POINTER = 1
+FA_ERR_BAD_SHAPE = 2
+FA_ERR_UNSUPPORTED_HEAD_DIM = 3
+FA_ERR_UNSUPPORTED_DTYPE = 4
+FA_ERR_UNSUPPORTED_LAYOUT = 5
+FA_ERR_UNSUPPORTED_DROPOUT = 6
+FA_ERR_BAD_SCALE = 7
+FA_ERR_MISALIGNED = 8
+FA_ERR_ALIASING = 9
+FA_ERR_HIP = 10
+
+FA_LAYOUT_BNSD = 0
+FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
+
+EXPORTS = ("fa_fwd", "fa_status_str", "fa_abi_version")
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A launch failure reported by the library (FA_ERR_HIP)."""
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa_mi355x.so and declare its C signatures."""
+    global _lib
+    if _lib is not None and path == LIB_PATH:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m attention_fa_fwd_07_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.fa_fwd.restype = ctypes.c_int
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp,            # q k v o lse
+                           i64, i64, i64, i64, i64,       # B H Sq Sk D
+                           ctypes.c_int, ctypes.c_float,  # layout scale
+                           ctypes.c_int, ctypes.c_float,  # causal keep_prob
+                           ctypes.c_int, ctypes.c_int,    # in_dtype o_dtype
+                           vp, vp, vp,                    # descale q k v
+                           vp]                            # stream
+    lib.fa_status_str.restype = ctypes.c_char_p
+    lib.fa_status_str.argtypes = [ctypes.c_int]
+    lib.fa_abi_version.restype = ctypes.c_int
+    lib.fa_abi_version.argtypes = []
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def status_str(code: int) -> str:
+    return load_library().fa_status_str(code).decode()
+
+
+def fa_fwd_raw(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_prob,
+               in_dtype, o_dtype, descale_q, descale_k, descale_v, stream) -> int:
+    """The C entry point with integer pointers; returns the status code."""
+    return load_library().fa_fwd(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale,
+                                 causal, keep_prob, in_dtype, o_dtype,
+                                 descale_q, descale_k, descale_v, stream)
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    table = {torch.float16: FA_F16, torch.bfloat16: FA_BF16,
+             torch.float8_e4m3fn: FA_FP8_E4M3, torch.float32: FA_F32}
+    if dt not in table:
+        raise ValueError(f"unsupported dtype {dt}")
+    return table[dt]
+
+
+def _check_status(code: int) -> None:
+    if code == FA_OK:
+        return
+    name = status_str(code)
+    if code == FA_ERR_HIP:
+        raise FaError(name)
+    raise ValueError(name)
+
+
+def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
+           keep_prob: float = 1.0, o_dtype=None, descale_q=None, descale_k=None,
+           descale_v=None, out=None, lse=None, stream=None):
+    """Attention forward over BNSD tensors on the GPU.
+
+    q [B,H,Sq,D], k/v [B,H,Sk,D] contiguous GPU tensors (fp16, bf16 or
+    float8_e4m3fn). fp8 inputs need ``descale_*``: one-element fp32 GPU
+    tensors (value = code * descale). Returns (o, lse): o [B,H,Sq,D] in
+    ``o_dtype`` (default: fp16 for fp16/fp8 inputs, bf16 for bf16 inputs),
+    lse [B,H,Sq] fp32 (natural-log logsumexp of the scaled, masked scores).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (BNSD)")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D):
+        raise ValueError("k and v must be [B, H, Sk, D] with q's B, H, D")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    in_code = _dtype_code(q.dtype)
+    if o_dtype is None:
+        o_dtype = torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float16
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, Sq, D), dtype=o_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
+    dq = descale_q.data_ptr() if descale_q is not None else None
+    dk = descale_k.data_ptr() if descale_k is not None else None
+    dv = descale_v.data_ptr() if descale_v is not None else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    code = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                      lse.data_ptr(), B, H, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale),
+                      1 if causal else 0, float(keep_prob), in_code,
+                      _dtype_code(out.dtype), dq, dk, dv, stream)
+    _check_status(code)
+    return out, lse

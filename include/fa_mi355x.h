@@ -1,0 +1,108 @@
+/*
+ * libfa_mi355x — FlashAttention forward for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes; no C++ or framework types cross it.
+ *
+ * What fa_fwd computes, per (batch b, head h) and query row i:
+ *
+ *   S_ij = scale * sum_d q[b,h,i,d] * k[b,h,j,d]
+ *   S_ij = -inf where causal and j > i           (top-left aligned)
+ *   O[b,h,i,:] = sum_j softmax_j(S_i.) * v[b,h,j,:]
+ *   lse[b,h,i] = ln sum_j exp(S_ij)              (natural log)
+ *
+ * The definition follows the PyTorch reference used for the correctness
+ * check in "ops-transformer FlashAttention on Ascend: build, run and tune"
+ * (ai6s.net/6a31724f..., section 4.3): scores scaled by `scale` before the
+ * mask, the strict upper triangle filled with -inf, softmax over keys, then
+ * the product with V. The call shape (q, k, v, head count, input_layout
+ * "BNSD", scale, keep_prob) is the one of npu_flash_attention in "Tracing
+ * npu_flash_attention through the CANN runtime" (ai6s.net/6a114bb2...,
+ * layer 1). The computation order is FlashAttention-2's: the outer loop runs
+ * over blocks of query rows, an online softmax keeps the running row maximum
+ * and row sum, and S and P never reach device memory (first page, section
+ * 1.2). The per-row logsumexp output is not defined on the pages; it is the
+ * natural-log logsumexp of the scaled, masked score row.
+ *
+ * Layout: contiguous BNSD. q and o: element (b,h,s,d) at ((b*H+h)*Sq+s)*D+d;
+ * k and v: ((b*H+h)*Sk+s)*D+d; lse: fp32 [B,H,Sq] at (b*H+h)*Sq+s. All
+ * offsets are computed in 64-bit integers.
+ *
+ * Supported (in_dtype -> o_dtype): F16 -> {F16, F32}; BF16 -> {BF16, F32};
+ * FP8_E4M3 -> {F16, F32}. Head dim D in {64, 128}. FP8_E4M3 is OCP e4m3fn;
+ * the value of an fp8 element is code * descale, with one fp32 descale per
+ * tensor (a device pointer to a single float, read with stride 0, as the
+ * fp8 scale tensors are broadcast in "Hygon FlashAttention: fixed-defect
+ * review", chatdocs.ruinique.com/hygon/flash-attention-fixed-bugs, item 17).
+ *
+ * Ownership: the caller owns every buffer. The library allocates and frees
+ * no device memory, never synchronises, and enqueues one kernel on `stream`
+ * before returning. q, k, v and the descales are read only; o and lse are
+ * written only in their valid region [B,H,Sq,D] and [B,H,Sq].
+ *
+ * Errors: fa_fwd returns a status code and never throws. On any error other
+ * than FA_ERR_HIP nothing is launched and the outputs are untouched.
+ *
+ * Thread safety: fa_fwd keeps no mutable state and may be called from
+ * several threads on different streams.
+ */
+#ifndef FA_MI355X_H
+#define FA_MI355X_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FA_ABI_VERSION 1
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1,         /* q, k, v, o or lse is NULL, or an fp8 descale is NULL */
+  FA_ERR_BAD_SHAPE = 2,            /* B, H, Sq or Sk < 1, or a size overflows 64-bit offsets or the grid */
+  FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* D not in {64, 128} */
+  FA_ERR_UNSUPPORTED_DTYPE = 4,    /* (in_dtype, o_dtype) pair not supported */
+  FA_ERR_UNSUPPORTED_LAYOUT = 5,   /* layout other than FA_LAYOUT_BNSD */
+  FA_ERR_UNSUPPORTED_DROPOUT = 6,  /* keep_prob != 1.0 (dropout is not implemented) */
+  FA_ERR_BAD_SCALE = 7,            /* scale is NaN or infinite */
+  FA_ERR_MISALIGNED = 8,           /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
+  FA_ERR_ALIASING = 9,             /* o or lse overlaps q, k, v, or each other */
+  FA_ERR_HIP = 10                  /* the kernel launch failed */
+} fa_status_t;
+
+typedef enum { FA_LAYOUT_BNSD = 0 } fa_layout_t;
+
+typedef enum { FA_F16 = 0, FA_BF16 = 1, FA_FP8_E4M3 = 2, FA_F32 = 3 } fa_dtype_t;
+
+/*
+ * fa_fwd — attention forward on one GPU.
+ *
+ * q [B,H,Sq,D], k [B,H,Sk,D], v [B,H,Sk,D] in in_dtype (device pointers);
+ * o [B,H,Sq,D] in o_dtype and lse [B,H,Sq] fp32 (device pointers, written).
+ * scale: any finite float (the configurations use 1/sqrt(D)).
+ * causal: 0 = no mask; any other value = top-left causal mask (key j is
+ *   visible to query i iff j <= i), so every row has at least one key.
+ * keep_prob: must be 1.0.
+ * descale_q/k/v: device pointers to one fp32 each for FA_FP8_E4M3 inputs;
+ *   ignored (may be NULL) otherwise.
+ * stream: HIP stream to enqueue on (0 = the null stream).
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                   fa_layout_t layout, float scale, int causal, float keep_prob,
+                   fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                   const float* descale_q, const float* descale_k, const float* descale_v,
+                   hipStream_t stream);
+
+/* Human-readable name of a status code ("FA_OK", ...); never NULL. */
+const char* fa_status_str(fa_status_t s);
+
+/* FA_ABI_VERSION of the built library. */
+int fa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_MI355X_H */

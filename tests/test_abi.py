@@ -1,0 +1,106 @@
+"""The C ABI without a GPU: the library loads, exports what the header
+declares, and rejects bad arguments before any HIP call (nothing launched)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import attention_fa_fwd_07_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa_mi355x.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_expected_entry_points():
+    assert declared_functions() == sorted(fa.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = fa.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in declared_functions():
+        assert name in syms
+
+
+def test_library_holds_gfx950_code():
+    blob = open(fa.LIB_PATH, "rb").read()
+    assert b"gfx950" in blob
+
+
+def test_abi_version_and_status_strings():
+    lib = fa.load_library()
+    assert lib.fa_abi_version() == 1
+    names = [fa.status_str(c) for c in range(11)]
+    assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP"
+    assert len(set(names)) == 11
+    assert fa.status_str(99) == "FA_ERR_UNKNOWN"
+
+
+# fake but aligned, non-overlapping "device" addresses: never dereferenced,
+# because every case below fails validation before any HIP call.
+Q, K, V, O, L = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+DQ, DK, DV = 0x60000000, 0x60000100, 0x60000200
+
+
+def call(**over):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=64, Sk=64, D=128,
+             layout=fa.FA_LAYOUT_BNSD, scale=0.125, causal=0, keep_prob=1.0,
+             in_dtype=fa.FA_F16, o_dtype=fa.FA_F16, descale_q=None, descale_k=None,
+             descale_v=None, stream=None)
+    a.update(over)
+    return fa.fa_fwd_raw(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(k=None), fa.FA_ERR_NULL_POINTER),
+    (dict(v=None), fa.FA_ERR_NULL_POINTER),
+    (dict(o=None), fa.FA_ERR_NULL_POINTER),
+    (dict(lse=None), fa.FA_ERR_NULL_POINTER),
+    (dict(B=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(H=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(Sq=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(Sk=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(B=1 << 30, H=1 << 30), fa.FA_ERR_BAD_SHAPE),
+    (dict(Sq=1 << 41), fa.FA_ERR_BAD_SHAPE),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(D=256), fa.FA_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(o_dtype=fa.FA_BF16), fa.FA_ERR_UNSUPPORTED_DTYPE),
+    (dict(in_dtype=fa.FA_BF16, o_dtype=fa.FA_F16), fa.FA_ERR_UNSUPPORTED_DTYPE),
+    (dict(in_dtype=fa.FA_F32, o_dtype=fa.FA_F32), fa.FA_ERR_UNSUPPORTED_DTYPE),
+    (dict(in_dtype=fa.FA_FP8_E4M3, o_dtype=fa.FA_F16), fa.FA_ERR_NULL_POINTER),
+    (dict(in_dtype=fa.FA_FP8_E4M3, o_dtype=fa.FA_BF16, descale_q=DQ, descale_k=DK,
+          descale_v=DV), fa.FA_ERR_UNSUPPORTED_DTYPE),
+    (dict(layout=1), fa.FA_ERR_UNSUPPORTED_LAYOUT),
+    (dict(keep_prob=0.9), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
+    (dict(scale=float("inf")), fa.FA_ERR_BAD_SCALE),
+    (dict(q=Q + 8), fa.FA_ERR_MISALIGNED),
+    (dict(o=O + 2), fa.FA_ERR_MISALIGNED),
+    (dict(lse=L + 2), fa.FA_ERR_MISALIGNED),
+    (dict(o=Q + 64), fa.FA_ERR_ALIASING),
+    (dict(o=V), fa.FA_ERR_ALIASING),
+    (dict(lse=K + 1024), fa.FA_ERR_ALIASING),
+    (dict(lse=O + 256), fa.FA_ERR_ALIASING),
+])
+def test_rejects_before_launch(over, code):
+    assert call(**over) == code
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(x, x, x)

@@ -1,0 +1,80 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.
+
+* edge sweep: tiny and ragged lengths around the 64/128 tile edges, Sq != Sk,
+  both head dims, both masks, both 16-bit input types, f32 and native O;
+* the five workloads at their full sizes, in the launch configuration the
+  benchmark times: whole heads and sampled rows against the oracle, and
+  properties that hold at any size for every row.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fa_inputs as fi
+from parity_util import compare, oracle_full, oracle_rows, run_gpu, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+LENGTHS = [(1, 1), (2, 2), (63, 63), (64, 64), (65, 65), (127, 127), (128, 128),
+           (129, 129), (255, 255), (257, 257), (100, 300), (300, 100), (1, 200),
+           (200, 1), (130, 513)]
+
+
+@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_edge_sweep(dtype, D, causal):
+    native = fi.BF16 if dtype == fi.BF16 else fi.F16
+    for i, (Sq, Sk) in enumerate(LENGTHS):
+        cfg = fi.Config("edge", 1, 2, Sq, Sk, D, dtype, causal, seed=500 + i)
+        inp = fi.make_inputs(cfg)
+        ref_o, ref_l = oracle_full(cfg, inp)
+        for od in (fi.F32, native):
+            o, lse = run_gpu(cfg, inp, od)
+            compare(cfg, od, o, lse, ref_o, ref_l, what=f"{dtype} D{D} c{causal} {Sq}x{Sk} {od}")
+
+
+def test_scale_variants():
+    """Negative and zero scale (zero: uniform weights over the visible keys)."""
+    for scale in (-0.3, 0.0, 2.0):
+        for causal in (False, True):
+            cfg = fi.Config("scale", 1, 2, 77, 77, 64, fi.F16, causal, seed=9, scale=scale)
+            inp = fi.make_inputs(cfg)
+            ref_o, ref_l = oracle_full(cfg, inp)
+            o, lse = run_gpu(cfg, inp, fi.F32)
+            compare(cfg, fi.F32, o, lse, ref_o, ref_l, what=f"scale {scale} c{causal}")
+
+
+def _heads_to_check(cfg, rng):
+    bh = [(0, 0), (cfg.B - 1, cfg.H - 1)]
+    extra = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H))) for _ in range(4)]
+    return bh, extra
+
+
+@pytest.mark.parametrize("idx", range(len(fi.CONFIGS)), ids=[c.name for c in fi.CONFIGS])
+def test_workload_full_size(idx):
+    cfg = fi.CONFIGS[idx]
+    if cfg.dtype == fi.FP8:
+        pytest.skip("fp8 e4m3 kernels are not built yet")
+    inp = fi.make_inputs(cfg)
+    rng = np.random.default_rng(idx)
+    whole, sampled = _heads_to_check(cfg, rng)
+    for od in (fi.F32, cfg.o_dtype):
+        o, lse = run_gpu(cfg, inp, od)
+        # properties at every row: finite, lse >= the scaled score of key 0
+        # (key 0 is visible to every row under either mask)
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+        q0 = fi.as_float64(inp.q[..., :, :], inp.descale_q)
+        k0 = fi.as_float64(inp.k[..., :1, :], inp.descale_k)
+        s0 = np.einsum("bhsd,bhd->bhs", q0, k0[:, :, 0, :]) * cfg.scale
+        assert np.all(lse >= s0 - 1e-3)
+        for (b, h) in whole:
+            rows = np.arange(cfg.Sq)
+            ro, rl = oracle_rows(cfg, inp, b, h, rows)
+            compare(cfg, od, o[b, h], lse[b, h], ro, rl, what=f"{cfg.name} {od} head {b},{h}")
+        for (b, h) in sampled:
+            rows = sample_rows(cfg.Sq, rng)
+            ro, rl = oracle_rows(cfg, inp, b, h, rows)
+            compare(cfg, od, o[b, h, rows], lse[b, h, rows], ro, rl,
+                    what=f"{cfg.name} {od} rows of {b},{h}")
