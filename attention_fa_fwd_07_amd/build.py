@@ -25,6 +25,8 @@ FLAGS = [
     "-fno-fast-math",
     # no packed fp32 arithmetic (v_pk_{add,mul,fma}_f32) in generated code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: no AGPR copies around the O rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Rpass-analysis=kernel-resource-usage",
 ]
 

@@ -91,21 +91,34 @@ __device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f
   }
 }
 
-// Two fp32 -> packed 16-bit, round to nearest even.
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed 16-bit, round to nearest even (v_cvt_pk_{f16,bf16}_f32).
 template <int KIND>
 __device__ __forceinline__ uint32_t pack2(float x, float y) {
+  uint32_t u;
   if constexpr (KIND == KBF16) {
-    __bf16 a = (__bf16)x, b = (__bf16)y;
-    uint16_t ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    const bf16x2_t v = {(__bf16)x, (__bf16)y};
+    __builtin_memcpy(&u, &v, 4);
   } else {
-    _Float16 a = (_Float16)x, b = (_Float16)y;
-    uint16_t ua, ub;
-    __builtin_memcpy(&ua, &a, 2);
-    __builtin_memcpy(&ub, &b, 2);
-    return (uint32_t)ua | ((uint32_t)ub << 16);
+    const half2_t v = {(_Float16)x, (_Float16)y};
+    __builtin_memcpy(&u, &v, 4);
+  }
+  return u;
+}
+
+// acc + a.lo + a.hi for a packed pair of 16-bit values (v_dot2c_f32_*).
+template <int KIND>
+__device__ __forceinline__ float add_pair(uint32_t a, float acc) {
+  if constexpr (KIND == KBF16) {
+    bf16x2_t x, one = {(__bf16)1.0f, (__bf16)1.0f};
+    __builtin_memcpy(&x, &a, 4);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+  } else {
+    half2_t x, one = {(_Float16)1.0f, (_Float16)1.0f};
+    __builtin_memcpy(&x, &a, 4);
+    return __builtin_amdgcn_fdot2(x, one, acc, false);
   }
 }
 
@@ -288,70 +301,84 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(Params p) {
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      u32x4 kf[NDS];
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) kf[ds] = *(const u32x4*)(kb_lds + kb * 32 * C * 16 + koffs[ds]);
       s[kb] = (f32x16){};
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) {
-        const u32x4 a = *(const u32x4*)(kb_lds + kb * 32 * C * 16 + koffs[ds]);
-        s[kb] = mfma32<KIND>(a, qf[ds], s[kb]);
-      }
+      for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma32<KIND>(kf[ds], qf[ds], s[kb]);
     }
 
-    // ---- masks: keys past Sk, keys above the diagonal ----
+    // ---- masks: keys past Sk, keys above the diagonal (32-bit, tile-relative) ----
     const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > q0 + wave * 32);
     if (need_mask) {
+      const int64_t kv = Sk - kt0;                        // valid keys in this tile (may exceed BN)
+      const int kvalid = kv < BN ? (int)kv : BN;
+      const int64_t qr = qrow - kt0;                      // last visible key, tile-relative
+      const int qlim = CAUSAL ? (qr < BN ? (int)qr : BN) : BN;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int64_t key = kt0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool dead = (key >= Sk) || (CAUSAL && key > qrow);
+          const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool dead = (key >= kvalid) || (key > qlim);
           s[kb][r] = dead ? -INFINITY : s[kb][r];
         }
       }
     }
 
     // ---- online softmax (log2 domain) ----
+    // The running maximum only moves when the tile's maximum exceeds it by
+    // more than 2^8 (in any lane of the wave): P is then bounded by 256, which
+    // fp16, bf16 and the fp32 accumulators hold exactly as well as values
+    // below 1, and the rescale of O is skipped on almost every tile. The
+    // final O / l and lse do not depend on which reference maximum was used.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = wave_max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;   // guard: no (-inf) - (-inf)
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
+    const float m_cand = fmaxf(m_run, mx * c);
+    const bool grow = m_cand > m_run + 8.0f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_use = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_cand;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+    }
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-    float rowsum = 0.f;
     u32x4 pf[NKB * 2];                    // P^T operand, one per 16-key step
     u32x4 pl[SPLIT_P ? NKB * 2 : 1];      // bf16 only: rounding residual of P
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float pv[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_use));
-        rowsum += pv[r];
-      }
+      for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_use));
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4 f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) f[e] = pack2<KIND>(pv[8 * half + 2 * e], pv[8 * half + 2 * e + 1]);
+        for (int e = 0; e < 4; ++e) {
+          f[e] = pack2<KIND>(pv[8 * half + 2 * e], pv[8 * half + 2 * e + 1]);
+          l_run = add_pair<KIND>(f[e], l_run);     // l sums the P that multiplies V
+        }
         pf[kb * 2 + half] = f;
         if constexpr (SPLIT_P) {
           u32x4 g;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
+          for (int e = 0; e < 4; ++e) {
             g[e] = pack2<KIND>(pv[8 * half + 2 * e] - unpack_lo<KIND>(f[e]),
                                pv[8 * half + 2 * e + 1] - unpack_hi<KIND>(f[e]));
+            l_run = add_pair<KIND>(g[e], l_run);
+          }
           pl[kb * 2 + half] = g;
         }
       }
     }
-    l_run = l_run * alpha + rowsum;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll

@@ -1,0 +1,196 @@
+"""Benchmark: attention forward TFLOP/s and fraction of the MI355X dense fp16
+MFMA peak on B4 H32 Sq=Sk=4096 D128 fp16, BNSD, non-causal, one GPU.
+
+One step = one fa_fwd call over the whole batch (inputs resident in HBM).
+Prints one JSON line. Options:
+  --gpus N      only N=1 is supported (one process, one GPU)
+  --steps K     timed steps (default 20)
+  --warmup W    untimed steps first (default 3)
+  --workload I  index into the workload list (default: the headline, 2)
+  --no-cpu      skip the CPU-oracle baseline leg
+  --cpu-seconds approximate CPU budget for the oracle leg (default 15)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8_e4m3": 5033.2}   # dense MFMA, MI355X
+HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_b4h32s4096d128_f16_traffic.json")
+KERNEL_SRC = os.path.join(ROOT, "attention_fa_fwd_07_amd", "csrc", "fa_fwd.hip")
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def device_info():
+    import ctypes
+    import torch
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "cus": props.multi_processor_count,
+            "arch": getattr(props, "gcnArchName", "")}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate = 5 (kHz)
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:
+            info["sclk_mhz"] = v.value / 1000.0
+    except OSError:
+        pass
+    return info
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    valid only for the kernel source it was measured on."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    d = json.load(open(TRAFFIC_FILE))
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(cfg, inp, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of whole heads."""
+    import numpy as np
+    import fa_inputs as fi
+    from oracle import head_forward
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    heads = 0
+    t0 = time.perf_counter()
+    bh = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    while heads < len(bh):
+        b, h = bh[heads]
+        q = fi.as_float64(inp.q[b, h], inp.descale_q)
+        k = fi.as_float64(inp.k[b, h], inp.descale_k)
+        v = fi.as_float64(inp.v[b, h], inp.descale_v)
+        head_forward(q, k, v, cfg.scale, cfg.causal)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = cfg.flops() * heads / (cfg.B * cfg.H)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{heads} of {cfg.B * cfg.H} heads of {cfg.name}, fp64 numpy, "
+                      f"{dt:.1f} s; value = algorithmic FLOP of the sample / wall time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a 512 MiB device-to-device copy (reference kernel "
+                         "of known traffic for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the attention forward here is a "
+              "single-GPU kernel (heads shard across GPUs without communication; "
+              "no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.calibrate_copy:
+        n = 512 << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+    import attention_fa_fwd_07_amd as fa
+    import fa_inputs as fi
+
+    cfg = fi.CONFIGS[args.workload]
+    inp = fi.make_inputs(cfg)
+    dev = torch.device("cuda:0")
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    kw = {}
+    if cfg.dtype == fi.FP8:
+        kw = {n: torch.tensor([d], dtype=torch.float32, device=dev) for n, d in
+              (("descale_q", inp.descale_q), ("descale_k", inp.descale_k),
+               ("descale_v", inp.descale_v))}
+    o = torch.empty(tuple(q.shape), dtype=fi.TORCH_DTYPE[cfg.o_dtype], device=dev)
+    lse = torch.empty(tuple(q.shape[:3]), dtype=torch.float32, device=dev)
+
+    def step():
+        fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_launch_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    avg_ms = statistics.fmean(per_launch_ms)
+    med_ms = statistics.median(per_launch_ms)
+    ms_per_step = wall / args.steps * 1e3
+
+    flops = cfg.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg.dtype]
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(),
+                "kernel": "fa_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
+                "median_launch_ms": round(med_ms, 4), "min_launch_ms": round(min(per_launch_ms), 4)}
+
+    out = {
+        "metric": "attn fwd TFLOP/s + % fp16 MFMA peak, B4 H32 S4096 D128 fp16 (1 GPU)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "pct_peak": round(100 * value / peak, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded N(0,1), BNSD)",
+        "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Sq": cfg.Sq, "Sk": cfg.Sk,
+                   "D": cfg.D, "causal": cfg.causal, "in_dtype": cfg.dtype,
+                   "o_dtype": cfg.o_dtype, "layout": "BNSD", "flop_per_step": flops},
+        "roofline": roofline,
+        "device": device_info(),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
