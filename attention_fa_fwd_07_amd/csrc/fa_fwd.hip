@@ -162,6 +162,28 @@ __device__ __forceinline__ int swz_v(int r) {
   else return ((r >> 1) & 1) << 2;
 }
 
+// 16 bytes per lane from base + voff (HBM) to LDS at lds_wave + 16 * lane
+// (global_load_lds_dwordx4). One asm statement sets M0 (the LDS destination,
+// wave-uniform), waits the one wait state the hardware needs between an M0
+// write and an LDS-DMA load, issues the load and restores M0, so the
+// compiler's view of M0 stays valid and it does not treat later LDS reads
+// as dependent on this load: the kernel waits for these loads explicitly
+// (s_waitcnt vmcnt) and orders them against LDS readers with barriers.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_wave) {
+  uint32_t saved;
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds_wave)
+      : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ float wave_max_halves(float x) {
   // After the swap each lane holds its own value and its partner's (l ^ 32).
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -181,228 +203,347 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   return xcd * base + (xcd < rem ? xcd : rem) + local;
 }
 
-template <int D, int BN, bool CAUSAL, int KIND, int OUT>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(Params p) {
-  constexpr int BM = 128;
-  constexpr int C = D / 8;                 // 16-byte chunks per row
-  constexpr int TILE = BN * D * 2;         // bytes of one K or V tile
-  constexpr int NDS = D / 16;              // k-steps of the first product
-  constexpr int NKB = BN / 32;             // 32-key blocks per tile
-  constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O
-  constexpr int LOADS = BN * C / 256;      // 16-byte loads per thread per tile
-  constexpr bool SPLIT_P = (KIND == KBF16);  // bf16: P = hi + lo
-  static_assert(LOADS * 256 == BN * C, "tile must split evenly over 256 lanes");
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// (lgkmcnt) but not for its HBM->LDS loads, which are waited for explicitly
+// (wait_loads) two blocks after they are issued. The scheduling fences keep
+// the compiler from moving instructions across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Wait until at most N of this wave's HBM->LDS loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
-  __shared__ __attribute__((aligned(1024))) char smem[4 * TILE];  // K0 K1 V0 V1
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) T*)(uintptr_t)addr;
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hl = lane >> 5;     // lane half
-  const int l32 = lane & 31;
+// One workgroup: 4 waves (256 lanes), BM = 128 query rows, 32 per wave.
+// Keys and values stream through LDS in stages of BN = 64 rows (two stage
+// buffers each for K and V); each wave works through them in 32-key blocks
+// with a software pipeline: while the MFMAs of S_{b+1} = K_{b+1} Q^T run,
+// the VALU computes the softmax of S_b; while the MFMAs of
+// O += V_b^T P_b^T run, the VALU masks S_{b+1} and finds its row maximum.
+// The block loop is unrolled by four (two stages), so that every LDS
+// address is a per-lane base plus a compile-time offset.
+template <int D, bool CAUSAL, int KIND, int OUT>
+struct FwdBlock {
+  static constexpr int BN = 64;                   // keys per LDS stage
+  static constexpr int BM = 128;                  // query rows per workgroup
+  static constexpr int NT = 256;                  // lanes per workgroup
+  static constexpr int C = D / 8;                 // 16-byte chunks per K/V row
+  static constexpr int TILE = BN * D * 2;         // bytes of one K or V stage buffer
+  static constexpr int BLK = 32 * C * 16;         // bytes of one 32-key block
+  static constexpr int NDS = D / 16;              // k-steps of S = K Q^T
+  static constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O
+  static constexpr int LOADS = BN * C / NT;       // 16-byte loads per lane, stage and tensor
+  static constexpr bool SPLIT_P = (KIND == KBF16);  // bf16: P = hi + lo
+  static constexpr int SMEM = 4 * TILE;           // K0 K1 V0 V1
+  static_assert(LOADS >= 1 && LOADS * NT == BN * C, "stage must split evenly over the lanes");
 
-  // ---- work decomposition (64-bit offsets) ----
-  const int t = xcd_remap(blockIdx.x, p.total);
-  const int bh = t / p.nqb;
-  int qb = t - bh * p.nqb;
-  if constexpr (CAUSAL) qb = p.nqb - 1 - qb;   // longest rows first
-  const int64_t Sq = p.Sq, Sk = p.Sk;
-  const int64_t q0 = (int64_t)qb * BM;
-  const int64_t in_elt = (KIND == KFP8) ? 1 : 2;
-  const char* qhead = p.q + (int64_t)bh * Sq * D * in_elt;
-  const char* khead = p.k + (int64_t)bh * Sk * D * in_elt;
-  const char* vhead = p.v + (int64_t)bh * Sk * D * in_elt;
+  const Params& p;
+  uint32_t lds0;                    // LDS byte address of the stage buffers
+  int tid, lane, wave, hl, l32;
+  int bh, NB, T, blast;
+  int64_t Sq, Sk, q0, qw0, qrow;
+  const char* khead;
+  const char* vhead;
+  float c;
 
-  const int64_t qrow = q0 + wave * 32 + l32;          // this lane's query
-  const int64_t qrow_ld = qrow < Sq ? qrow : Sq - 1;   // clamped for the load
-
-  // ---- Q fragments (B operand of S^T = K Q^T), kept in registers ----
   u32x4 qf[NDS];
-#pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) {
-    qf[ds] = *(const u32x4*)(qhead + (qrow_ld * D + ds * 16 + hl * 8) * 2);
-    if (p.negate) qf[ds] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-  }
-
-  // ---- tile range ----
-  int64_t kend = Sk;
-  if constexpr (CAUSAL) {
-    const int64_t last_q = q0 + BM - 1;
-    kend = last_q + 1 < Sk ? last_q + 1 : Sk;
-  }
-  const int ntiles = (int)((kend + BN - 1) / BN);
-
-  auto load_tile = [&](int j, int buf) {
-    const int64_t row0 = (int64_t)j * BN;
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int pidx = i * 256 + tid;       // physical chunk in the tile
-      const int r = pidx / C;
-      const int pc = pidx % C;
-      int64_t grow = row0 + r;
-      grow = grow < Sk ? grow : Sk - 1;
-      const int64_t koff = (grow * D + (pc ^ swz_k<D>(r)) * 8) * 2;
-      const int64_t voff = (grow * D + (pc ^ swz_v<D>(r)) * 8) * 2;
-      char* kdst = smem + buf * TILE + (i * 256 + wave * 64) * 16;
-      char* vdst = smem + (2 + buf) * TILE + (i * 256 + wave * 64) * 16;
-      __builtin_amdgcn_global_load_lds((const void*)(khead + koff), LDS_PTR(void, kdst), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(vhead + voff), LDS_PTR(void, vdst), 16, 0, 0);
-    }
-  };
-
-  // ---- per-lane LDS read offsets (loop invariant) ----
-  // K: lane reads row kb*32 + l32, logical chunk 2*ds + hl.
-  int koffs[NDS];
-#pragma unroll
-  for (int ds = 0; ds < NDS; ++ds) koffs[ds] = (l32 * C + ((2 * ds + hl) ^ swz_k<D>(l32))) * 16;
-  // V (transposing reads): within each 16-lane group, lane i supplies row
-  // 16*step + 4*hl + (i/4) [+8 for the second read] and head-dim columns
-  // 32*db + 16*((lane/16)&1) + 4*(i%4) .. +4; the read returns to lane i the
-  // four keys of its head-dim column.
-  const int gi = lane & 15;
-  const int vr = 4 * hl + (gi >> 2);
-  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);   // column within a 32-block
-  int voffs[NDB][2];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int r = vr + 8 * e;   // row within a 16-row step (swizzle is step invariant)
-      const int col = 32 * db + vcol;
-      voffs[db][e] = (r * C + ((col >> 3) ^ swz_v<D>(r))) * 16 + (col & 7) * 2;
-    }
-  }
-
-  // ---- accumulators ----
+  uint32_t kaddr[NDS];              // K fragment addresses (stage buffer 0, block 0)
+  uint32_t vaddr[NDB][2];           // V transposing-read addresses (stage buffer 0, block 0)
+  uint32_t goff_k[LOADS], goff_v[LOADS];   // this lane's byte offsets in a full stage
   f32x16 acc_o[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
-  float m_run = -INFINITY;   // running max of scaled scores, log2 units
-  float l_run = 0.f;         // this lane's partial row sum (16 of the 32 rows per block)
-  const float c = p.scale_log2;
+  float m_run, l_run, alpha;
+  bool rescale;
+  u32x4 pf[2];                      // P^T operand of the two 16-key steps of a block
+  u32x4 pl[SPLIT_P ? 2 : 1];        // bf16 only: rounding residual of P
 
-  load_tile(0, 0);
+  __device__ __forceinline__ FwdBlock(const Params& pp, char* sm) : p(pp) {
+    lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, sm);
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    hl = lane >> 5;
+    l32 = lane & 31;
+    const int t = xcd_remap(blockIdx.x, p.total);
+    bh = t / p.nqb;
+    int qb = t - bh * p.nqb;
+    if constexpr (CAUSAL) qb = p.nqb - 1 - qb;   // longest rows first
+    Sq = p.Sq;
+    Sk = p.Sk;
+    q0 = (int64_t)qb * BM;
+    khead = p.k + (int64_t)bh * Sk * D * 2;
+    vhead = p.v + (int64_t)bh * Sk * D * 2;
+    qw0 = q0 + wave * 32;
+    qrow = qw0 + l32;
+    c = p.scale_log2;
 
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
-
-    const int64_t kt0 = (int64_t)j * BN;
-    // Causal: a wave whose rows all lie above this tile's first key has
-    // nothing to add (all its scores here are masked).
-    if (CAUSAL && kt0 > q0 + wave * 32 + 31) continue;
-
-    const char* kb_lds = smem + buf * TILE;
-    const char* vb_lds = smem + (2 + buf) * TILE;
-
-    // ---- S^T = K Q^T for NKB blocks of 32 keys ----
-    f32x16 s[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      u32x4 kf[NDS];
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) kf[ds] = *(const u32x4*)(kb_lds + kb * 32 * C * 16 + koffs[ds]);
-      s[kb] = (f32x16){};
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma32<KIND>(kf[ds], qf[ds], s[kb]);
+    // 32-key blocks: the workgroup's count, and the last one this wave needs
+    int64_t kend = Sk;
+    if constexpr (CAUSAL) kend = (q0 + BM) < Sk ? (q0 + BM) : Sk;
+    NB = (int)((kend + 31) / 32);
+    T = (NB + 1) >> 1;
+    blast = NB - 1;
+    if constexpr (CAUSAL) {
+      const int64_t bl = (qw0 + 31) / 32;
+      blast = bl < blast ? (int)bl : blast;
     }
 
-    // ---- masks: keys past Sk, keys above the diagonal (32-bit, tile-relative) ----
-    const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > q0 + wave * 32);
-    if (need_mask) {
-      const int64_t kv = Sk - kt0;                        // valid keys in this tile (may exceed BN)
-      const int kvalid = kv < BN ? (int)kv : BN;
-      const int64_t qr = qrow - kt0;                      // last visible key, tile-relative
-      const int qlim = CAUSAL ? (qr < BN ? (int)qr : BN) : BN;
+    // Q fragments (B operand of S^T = K Q^T), kept in registers; rows past
+    // Sq read the last row (their results are never stored)
+    const char* qhead = p.q + (int64_t)bh * Sq * D * 2;
+    const int64_t qrow_ld = qrow < Sq ? qrow : Sq - 1;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int ds = 0; ds < NDS; ++ds) {
+      qf[ds] = *(const u32x4*)(qhead + (qrow_ld * D + ds * 16 + hl * 8) * 2);
+      if (p.negate) qf[ds] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+    }
+
+    // K (ds_read_b128): row l32 of a 32-key block, logical chunk 2*ds + hl,
+    // stored at chunk (2*ds + hl) ^ swz_k(row).
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool dead = (key >= kvalid) || (key > qlim);
-          s[kb][r] = dead ? -INFINITY : s[kb][r];
-        }
+    for (int ds = 0; ds < NDS; ++ds)
+      kaddr[ds] = lds0 + l32 * C * 16 + (((2 * ds + hl) ^ swz_k<D>(l32)) << 4);
+    // V (ds_read_b64_tr_b16): within each 16-lane group, lane i supplies row
+    // 16*step + 4*hl + (i/4) [+8 for the second read] and head-dim columns
+    // 32*db + 16*((lane/16)&1) + 4*(i%4) .. +4; the read returns to lane i the
+    // four keys of its head-dim column. The swizzle of a row only depends on
+    // its index mod 16, so one address per (db, read) serves every step.
+    const int gi = lane & 15;
+    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int r = 4 * hl + (gi >> 2) + 8 * e;
+        const int col = 32 * db + vcol;
+        vaddr[db][e] = lds0 + 2 * TILE + (r * C + ((col >> 3) ^ swz_v<D>(r))) * 16 + (col & 7) * 2;
       }
     }
+    // HBM->LDS: lane chunk i*NT + tid of a stage; one wave writes a
+    // contiguous KiB of LDS per instruction, so the swizzle is applied to
+    // the global source offset.
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int pidx = i * NT + tid;
+      const int r = pidx / C;
+      const int pc = pidx % C;
+      goff_k[i] = (uint32_t)((r * D + (pc ^ swz_k<D>(r)) * 8) * 2);
+      goff_v[i] = (uint32_t)((r * D + (pc ^ swz_v<D>(r)) * 8) * 2);
+    }
 
-    // ---- online softmax (log2 domain) ----
-    // The running maximum only moves when the tile's maximum exceeds it by
-    // more than 2^8 (in any lane of the wave): P is then bounded by 256, which
-    // fp16, bf16 and the fp32 accumulators hold exactly as well as values
-    // below 1, and the rescale of O is skipped on almost every tile. The
-    // final O / l and lse do not depend on which reference maximum was used.
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
+    m_run = -INFINITY;
+    l_run = 0.f;
+    rescale = false;
+    alpha = 1.f;
+  }
+
+  // ---- HBM -> LDS: one stage (64 rows) of K or V ----
+  // Rows past Sk read the last row (only the final stage can have them).
+  template <bool IS_V>
+  __device__ __forceinline__ void load_stage(int t, int buf) {
+    const int64_t row0 = (int64_t)t * BN;
+    const char* base = (IS_V ? vhead : khead) + row0 * (D * 2);
+    const uint32_t dst = lds0 + (IS_V ? 2 * TILE : 0) + buf * TILE + wave * 64 * 16;
+    const int64_t left = Sk - 1 - row0;
+    if (left >= BN - 1) {
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) dma16(base, IS_V ? goff_v[i] : goff_k[i], dst + i * NT * 16);
+    } else {
+      const int rmax = (int)left;
+#pragma unroll
+      for (int i = 0; i < LOADS; ++i) {
+        const int pidx = i * NT + tid;
+        const int r = pidx / C;
+        const int pc = pidx % C;
+        const int rr = r < rmax ? r : rmax;
+        const int sw = IS_V ? swz_v<D>(r) : swz_k<D>(r);
+        dma16(base, (uint32_t)((rr * D + (pc ^ sw) * 8) * 2), dst + i * NT * 16);
+      }
+    }
+  }
+
+  // ---- S = K Q^T for one 32-key block (OFF: its byte offset in the K buffers) ----
+  template <int OFF>
+  __device__ __forceinline__ void gemm_s(f32x16& acc) {
+    u32x4 kf[NDS];
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) kf[ds] = lds_load<u32x4>(kaddr[ds] + OFF);
+    acc = (f32x16){};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) acc = mfma32<KIND>(kf[ds], qf[ds], acc);
+  }
+
+  // ---- O += V^T P^T for one 32-key block (OFF: its byte offset in the V buffers) ----
+  template <int OFF>
+  __device__ __forceinline__ void gemm_pv() {
+#pragma unroll
+    for (int t2 = 0; t2 < 2; ++t2) {
+      u32x4 vf[NDB];
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        u32x2 y[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const fp16x4_tr x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+              (__attribute__((address_space(3))) fp16x4_tr*)(uintptr_t)(vaddr[db][e] + OFF + t2 * 16 * C * 16));
+          __builtin_memcpy(&y[e], &x, 8);
+        }
+        vf[db] = (u32x4){y[0][0], y[0][1], y[1][0], y[1][1]};
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        acc_o[db] = mfma32<KIND>(vf[db], pf[t2], acc_o[db]);
+        if constexpr (SPLIT_P) acc_o[db] = mfma32<KIND>(vf[db], pl[t2], acc_o[db]);
+      }
+    }
+  }
+
+  // ---- mask and row maximum of S_b; new running maximum ----
+  // The running maximum of each row is kept exactly (the largest P of a row
+  // is then exactly 1); when it moves in some lane of the wave, O and l are
+  // rescaled by exp2(m_old - m_new) before block b's contribution is added.
+  __device__ __forceinline__ void mask_max(f32x16& sb, int b) {
+    const int64_t kt0 = (int64_t)b * 32;
+    const bool need_mask = (kt0 + 32 > Sk) || (CAUSAL && kt0 + 31 > qw0);
+    if (need_mask) {
+      // key = kt0 + 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or above
+      // this row's diagonal: compare the compile-time part with a per-lane limit
+      const int64_t kv = Sk - kt0;
+      int lim = kv < 32 ? (int)kv : 32;
+      if constexpr (CAUSAL) {
+        const int64_t qr = qrow - kt0 + 1;
+        lim = qr < lim ? (int)qr : lim;
+      }
+      lim -= 4 * hl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sb[r] = (8 * (r >> 2) + (r & 3)) >= lim ? -INFINITY : sb[r];
+    }
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[r]);
     mx = wave_max_halves(mx);
     const float m_cand = fmaxf(m_run, mx * c);
-    const bool grow = m_cand > m_run + 8.0f;
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run) != 0;
+    if (rescale) {
       const float m_use = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       m_run = m_cand;
+    }
+  }
+
+  // ---- apply a pending rescale of O and l ----
+  __device__ __forceinline__ void apply_rescale() {
+    if (rescale) {
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      rescale = false;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  }
 
-    u32x4 pf[NKB * 2];                    // P^T operand, one per 16-key step
-    u32x4 pl[SPLIT_P ? NKB * 2 : 1];      // bf16 only: rounding residual of P
+  // ---- P_b = exp2(S_b * c - m) as the 16-bit P^T operand; l += sum P ----
+  __device__ __forceinline__ void softmax_p(const f32x16& sb) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float pv[16];
+    for (int half = 0; half < 2; ++half) {
+      float pv[8];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_use));
+      for (int r = 0; r < 8; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[8 * half + r], c, -m_use));
+      u32x4 f;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 f;
+      for (int e = 0; e < 4; ++e) {
+        f[e] = pack2<KIND>(pv[2 * e], pv[2 * e + 1]);
+        l_run = add_pair<KIND>(f[e], l_run);     // l sums the P that multiplies V
+      }
+      pf[half] = f;
+      if constexpr (SPLIT_P) {
+        u32x4 g;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          f[e] = pack2<KIND>(pv[8 * half + 2 * e], pv[8 * half + 2 * e + 1]);
-          l_run = add_pair<KIND>(f[e], l_run);     // l sums the P that multiplies V
+          g[e] = pack2<KIND>(pv[2 * e] - unpack_lo<KIND>(f[e]), pv[2 * e + 1] - unpack_hi<KIND>(f[e]));
+          l_run = add_pair<KIND>(g[e], l_run);
         }
-        pf[kb * 2 + half] = f;
-        if constexpr (SPLIT_P) {
-          u32x4 g;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            g[e] = pack2<KIND>(pv[8 * half + 2 * e] - unpack_lo<KIND>(f[e]),
-                               pv[8 * half + 2 * e + 1] - unpack_hi<KIND>(f[e]));
-            l_run = add_pair<KIND>(g[e], l_run);
-          }
-          pl[kb * 2 + half] = g;
-        }
-      }
-    }
-
-    // ---- O^T += V^T P^T ----
-#pragma unroll
-    for (int st = 0; st < BN / 16; ++st) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const fp16x4_tr x0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            LDS_PTR(fp16x4_tr, vb_lds + st * 16 * C * 16 + voffs[db][0]));
-        const fp16x4_tr x1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-            LDS_PTR(fp16x4_tr, vb_lds + st * 16 * C * 16 + voffs[db][1]));
-        u32x2 y0, y1;
-        __builtin_memcpy(&y0, &x0, 8);
-        __builtin_memcpy(&y1, &x1, 8);
-        const u32x4 a = (u32x4){y0[0], y0[1], y1[0], y1[1]};
-        acc_o[db] = mfma32<KIND>(a, pf[st], acc_o[db]);
-        if constexpr (SPLIT_P) acc_o[db] = mfma32<KIND>(a, pl[st], acc_o[db]);
+        pl[half] = g;
       }
     }
   }
 
+  // One 32-key block b = 4u + K of the four-block loop body (K compile-time):
+  // S_{b+1} and softmax(S_b); O += V_b^T P_b^T and mask/max of S_{b+1};
+  // then the stage hand-off.
+  template <int K>
+  __device__ __forceinline__ void block_step(int b, f32x16& s_cur, f32x16& s_nxt, bool& issued_prev) {
+    constexpr int OFF_CUR = (K >> 1) * TILE + (K & 1) * BLK;            // block b in its stage buffer
+    constexpr int OFF_NXT = (((K + 1) >> 1) & 1) * TILE + ((K + 1) & 1) * BLK;
+    apply_rescale();
+    if (b + 1 <= blast) gemm_s<OFF_NXT>(s_nxt);
+    if (b <= blast) softmax_p(s_cur);
+    if (b <= blast) gemm_pv<OFF_CUR>();
+    if (b + 1 <= blast) mask_max(s_nxt, b + 1);
+
+    // Stage t = b / 2 lives in buffer t % 2. Its K rows are last read in
+    // iteration 2t (S_{2t+1}), its V rows in iteration 2t+1 (PV_{2t+1}).
+    // After the barrier that ends iteration 2t the K of stage t+2 is
+    // loaded, after the one that ends 2t+1 its V; each batch is waited for
+    // at the end of the iteration after next, before the barrier that
+    // precedes its first reader (S_{2t+4} in iteration 2t+3, PV_{2t+4} in
+    // iteration 2t+4).
+    if (issued_prev) wait_loads<LOADS>(); else wait_loads<0>();
+    lds_barrier();
+    const int t = b >> 1;
+    issued_prev = false;
+    if (t + 2 < T) {
+      if constexpr ((K & 1) == 0) load_stage<false>(t + 2, K >> 1);
+      else load_stage<true>(t + 2, K >> 1);
+      issued_prev = true;
+    }
+  }
+
+  __device__ __forceinline__ void run() {
+    load_stage<false>(0, 0);
+    load_stage<true>(0, 0);
+    if (T > 1) {
+      load_stage<false>(1, 1);
+      load_stage<true>(1, 1);
+    }
+    wait_loads<0>();
+    lds_barrier();
+
+    f32x16 s0, s1;
+    if (blast >= 0) {
+      gemm_s<0>(s0);
+      mask_max(s0, 0);
+    }
+    bool issued_prev = false;
+    for (int b0 = 0; b0 < NB; b0 += 4) {
+      block_step<0>(b0, s0, s1, issued_prev);
+      if (b0 + 1 >= NB) break;
+      block_step<1>(b0 + 1, s1, s0, issued_prev);
+      if (b0 + 2 >= NB) break;
+      block_step<2>(b0 + 2, s0, s1, issued_prev);
+      if (b0 + 3 >= NB) break;
+      block_step<3>(b0 + 3, s1, s0, issued_prev);
+    }
+    store();
+  }
+
   // ---- epilogue: O = O / l, lse = (m + log2 l) * ln 2 ----
-  const float l_tot = wave_sum_halves(l_run);
-  const float inv_l = 1.f / l_tot;
-  if (qrow < Sq) {
+  __device__ __forceinline__ void store() {
+    const float l_tot = wave_sum_halves(l_run);
+    const float inv_l = 1.f / l_tot;
+    if (qrow >= Sq) return;
     char* orow = p.o + ((int64_t)bh * Sq + qrow) * D * (OUT == OF32 ? 4 : 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
@@ -425,6 +566,14 @@ __global__ __launch_bounds__(256) void fa_fwd_kernel(Params p) {
       p.lse[(int64_t)bh * Sq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
     }
   }
+};
+
+template <int D, bool CAUSAL, int KIND, int OUT>
+__global__ __launch_bounds__(256) void fa_fwd_kernel(Params p) {
+  using Blk = FwdBlock<D, CAUSAL, KIND, OUT>;
+  __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
+  Blk blk(p, smem);
+  blk.run();
 }
 
 }  // namespace fa
@@ -438,7 +587,7 @@ typedef void (*KernelFn)(Params);
 
 template <int D, bool CAUSAL, int KIND, int OUT>
 KernelFn pick() {
-  return fa::fa_fwd_kernel<D, 64, CAUSAL, KIND, OUT>;
+  return fa::fa_fwd_kernel<D, CAUSAL, KIND, OUT>;
 }
 
 template <int D, int KIND, int OUT>
