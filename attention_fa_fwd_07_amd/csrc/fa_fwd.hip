@@ -205,18 +205,17 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
 // (lgkmcnt) but not for its HBM->LDS loads, which are waited for explicitly
-// (wait_loads) two blocks after they are issued. The scheduling fences keep
+// (wait_loads) one tile after they are issued. The scheduling fences keep
 // the compiler from moving instructions across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
-// Wait until at most N of this wave's HBM->LDS loads are outstanding.
-template <int N>
+// Wait until none of this wave's HBM->LDS loads is outstanding.
 __device__ __forceinline__ void wait_loads() {
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -226,48 +225,46 @@ __device__ __forceinline__ T lds_load(uint32_t addr) {
 }
 
 // One workgroup: 4 waves (256 lanes), BM = 128 query rows, 32 per wave.
-// Keys and values stream through LDS in stages of BN = 64 rows (two stage
-// buffers each for K and V); each wave works through them in 32-key blocks
-// with a software pipeline: while the MFMAs of S_{b+1} = K_{b+1} Q^T run,
-// the VALU computes the softmax of S_b; while the MFMAs of
-// O += V_b^T P_b^T run, the VALU masks S_{b+1} and finds its row maximum.
-// The block loop is unrolled by four (two stages), so that every LDS
-// address is a per-lane base plus a compile-time offset.
-template <int D, bool CAUSAL, int KIND, int OUT>
-struct FwdBlock {
-  static constexpr int BN = 64;                   // keys per LDS stage
+// Keys and values stream through LDS in tiles of BN = 64 rows, double
+// buffered: the loads of tile j+1 are issued right after the barrier that
+// opens tile j and waited for before the barrier that opens tile j+1. Per
+// tile each wave runs S^T = K Q^T (2 x D/16 MFMAs), the mask, the online
+// softmax and O^T += V^T P^T (4 x D/32 MFMAs); two waves share each SIMD,
+// so one wave's matrix products overlap the other's softmax.
+template <int D, int BN_, bool CAUSAL, int KIND, int OUT>
+struct FwdTile {
+  static constexpr int BN = BN_;                  // keys per tile
   static constexpr int BM = 128;                  // query rows per workgroup
   static constexpr int NT = 256;                  // lanes per workgroup
   static constexpr int C = D / 8;                 // 16-byte chunks per K/V row
-  static constexpr int TILE = BN * D * 2;         // bytes of one K or V stage buffer
-  static constexpr int BLK = 32 * C * 16;         // bytes of one 32-key block
+  static constexpr int TILE = BN * D * 2;         // bytes of one K or V tile buffer
   static constexpr int NDS = D / 16;              // k-steps of S = K Q^T
+  static constexpr int NKB = BN / 32;             // 32-key blocks per tile
   static constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O
-  static constexpr int LOADS = BN * C / NT;       // 16-byte loads per lane, stage and tensor
+  static constexpr int NST = BN / 16;             // 16-key steps of O += V^T P^T
+  static constexpr int LOADS = BN * C / NT;       // 16-byte loads per lane, tile and tensor
   static constexpr bool SPLIT_P = (KIND == KBF16);  // bf16: P = hi + lo
   static constexpr int SMEM = 4 * TILE;           // K0 K1 V0 V1
-  static_assert(LOADS >= 1 && LOADS * NT == BN * C, "stage must split evenly over the lanes");
+  static_assert(LOADS >= 1 && LOADS * NT == BN * C, "tile must split evenly over the lanes");
+  static_assert((NT / C) % 16 == 0, "swizzle period must divide the rows per load");
 
   const Params& p;
-  uint32_t lds0;                    // LDS byte address of the stage buffers
+  uint32_t lds0;                    // LDS byte address of the tile buffers
   int tid, lane, wave, hl, l32;
-  int bh, NB, T, blast;
+  int bh, ntiles;
   int64_t Sq, Sk, q0, qw0, qrow;
   const char* khead;
   const char* vhead;
   float c;
 
   u32x4 qf[NDS];
-  uint32_t kaddr[NDS];              // K fragment addresses (stage buffer 0, block 0)
-  uint32_t vaddr[NDB][2];           // V transposing-read addresses (stage buffer 0, block 0)
-  uint32_t goff_k[LOADS], goff_v[LOADS];   // this lane's byte offsets in a full stage
+  uint32_t kaddr[NDS];              // K fragment addresses (buffer 0, key block 0)
+  uint32_t vaddr[NDB][2];           // V transposing-read addresses (buffer 0, step 0)
+  uint32_t goff_k, goff_v;          // this lane's byte offsets in a full tile (first load)
   f32x16 acc_o[NDB];
-  float m_run, l_run, alpha;
-  bool rescale;
-  u32x4 pf[2];                      // P^T operand of the two 16-key steps of a block
-  u32x4 pl[SPLIT_P ? 2 : 1];        // bf16 only: rounding residual of P
+  float m_run, l_run;
 
-  __device__ __forceinline__ FwdBlock(const Params& pp, char* sm) : p(pp) {
+  __device__ __forceinline__ FwdTile(const Params& pp, char* sm) : p(pp) {
     lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, sm);
     tid = threadIdx.x;
     lane = tid & 63;
@@ -287,16 +284,9 @@ struct FwdBlock {
     qrow = qw0 + l32;
     c = p.scale_log2;
 
-    // 32-key blocks: the workgroup's count, and the last one this wave needs
     int64_t kend = Sk;
     if constexpr (CAUSAL) kend = (q0 + BM) < Sk ? (q0 + BM) : Sk;
-    NB = (int)((kend + 31) / 32);
-    T = (NB + 1) >> 1;
-    blast = NB - 1;
-    if constexpr (CAUSAL) {
-      const int64_t bl = (qw0 + 31) / 32;
-      blast = bl < blast ? (int)bl : blast;
-    }
+    ntiles = (int)((kend + BN - 1) / BN);
 
     // Q fragments (B operand of S^T = K Q^T), kept in registers; rows past
     // Sq read the last row (their results are never stored)
@@ -329,37 +319,39 @@ struct FwdBlock {
         vaddr[db][e] = lds0 + 2 * TILE + (r * C + ((col >> 3) ^ swz_v<D>(r))) * 16 + (col & 7) * 2;
       }
     }
-    // HBM->LDS: lane chunk i*NT + tid of a stage; one wave writes a
+    // HBM->LDS: lane chunk i*NT + tid of a tile; one wave writes a
     // contiguous KiB of LDS per instruction, so the swizzle is applied to
-    // the global source offset.
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-      const int pidx = i * NT + tid;
-      const int r = pidx / C;
-      const int pc = pidx % C;
-      goff_k[i] = (uint32_t)((r * D + (pc ^ swz_k<D>(r)) * 8) * 2);
-      goff_v[i] = (uint32_t)((r * D + (pc ^ swz_v<D>(r)) * 8) * 2);
+    // the global source offset. Load i covers rows r + i*NT/C; the swizzle
+    // only depends on the row mod 16, so every load of a lane uses the same
+    // chunk and the offsets differ by i*(NT/C) rows.
+    {
+      const int r = tid / C;
+      const int pc = tid % C;
+      goff_k = (uint32_t)((r * D + (pc ^ swz_k<D>(r)) * 8) * 2);
+      goff_v = (uint32_t)((r * D + (pc ^ swz_v<D>(r)) * 8) * 2);
     }
 
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
     m_run = -INFINITY;
     l_run = 0.f;
-    rescale = false;
-    alpha = 1.f;
   }
 
-  // ---- HBM -> LDS: one stage (64 rows) of K or V ----
-  // Rows past Sk read the last row (only the final stage can have them).
-  template <bool IS_V>
-  __device__ __forceinline__ void load_stage(int t, int buf) {
-    const int64_t row0 = (int64_t)t * BN;
-    const char* base = (IS_V ? vhead : khead) + row0 * (D * 2);
-    const uint32_t dst = lds0 + (IS_V ? 2 * TILE : 0) + buf * TILE + wave * 64 * 16;
+  // ---- HBM -> LDS: tile j of K and V into buffer buf ----
+  // Rows past Sk read the last row (only the final tile can have them).
+  __device__ __forceinline__ void load_tile(int j, int buf) {
+    const int64_t row0 = (int64_t)j * BN;
+    const char* kb = khead + row0 * (D * 2);
+    const char* vb = vhead + row0 * (D * 2);
+    const uint32_t kd = lds0 + buf * TILE + wave * 64 * 16;
+    const uint32_t vd = lds0 + (2 + buf) * TILE + wave * 64 * 16;
     const int64_t left = Sk - 1 - row0;
     if (left >= BN - 1) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) dma16(base, IS_V ? goff_v[i] : goff_k[i], dst + i * NT * 16);
+      for (int i = 0; i < LOADS; ++i) {
+        dma16(kb + i * (NT / C) * D * 2, goff_k, kd + i * NT * 16);
+        dma16(vb + i * (NT / C) * D * 2, goff_v, vd + i * NT * 16);
+      }
     } else {
       const int rmax = (int)left;
 #pragma unroll
@@ -368,173 +360,131 @@ struct FwdBlock {
         const int r = pidx / C;
         const int pc = pidx % C;
         const int rr = r < rmax ? r : rmax;
-        const int sw = IS_V ? swz_v<D>(r) : swz_k<D>(r);
-        dma16(base, (uint32_t)((rr * D + (pc ^ sw) * 8) * 2), dst + i * NT * 16);
+        dma16(kb, (uint32_t)((rr * D + (pc ^ swz_k<D>(r)) * 8) * 2), kd + i * NT * 16);
+        dma16(vb, (uint32_t)((rr * D + (pc ^ swz_v<D>(r)) * 8) * 2), vd + i * NT * 16);
       }
     }
   }
 
-  // ---- S = K Q^T for one 32-key block (OFF: its byte offset in the K buffers) ----
-  template <int OFF>
-  __device__ __forceinline__ void gemm_s(f32x16& acc) {
-    u32x4 kf[NDS];
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) kf[ds] = lds_load<u32x4>(kaddr[ds] + OFF);
-    acc = (f32x16){};
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) acc = mfma32<KIND>(kf[ds], qf[ds], acc);
-  }
+  // ---- one tile: S, mask, online softmax, O += V^T P^T ----
+  __device__ __forceinline__ void tile(int j, int buf) {
+    const int64_t kt0 = (int64_t)j * BN;
+    const uint32_t koff = buf * TILE;
 
-  // ---- O += V^T P^T for one 32-key block (OFF: its byte offset in the V buffers) ----
-  template <int OFF>
-  __device__ __forceinline__ void gemm_pv() {
+    // S^T = K Q^T for NKB blocks of 32 keys
+    f32x16 s[NKB];
 #pragma unroll
-    for (int t2 = 0; t2 < 2; ++t2) {
-      u32x4 vf[NDB];
+    for (int kb = 0; kb < NKB; ++kb) {
+      u32x4 kf[NDS];
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x2 y[2];
+      for (int ds = 0; ds < NDS; ++ds) kf[ds] = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * C * 16);
+      s[kb] = (f32x16){};
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const fp16x4_tr x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-              (__attribute__((address_space(3))) fp16x4_tr*)(uintptr_t)(vaddr[db][e] + OFF + t2 * 16 * C * 16));
-          __builtin_memcpy(&y[e], &x, 8);
-        }
-        vf[db] = (u32x4){y[0][0], y[0][1], y[1][0], y[1][1]};
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        acc_o[db] = mfma32<KIND>(vf[db], pf[t2], acc_o[db]);
-        if constexpr (SPLIT_P) acc_o[db] = mfma32<KIND>(vf[db], pl[t2], acc_o[db]);
-      }
+      for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma32<KIND>(kf[ds], qf[ds], s[kb]);
     }
-  }
 
-  // ---- mask and row maximum of S_b; new running maximum ----
-  // The running maximum of each row is kept exactly (the largest P of a row
-  // is then exactly 1); when it moves in some lane of the wave, O and l are
-  // rescaled by exp2(m_old - m_new) before block b's contribution is added.
-  __device__ __forceinline__ void mask_max(f32x16& sb, int b) {
-    const int64_t kt0 = (int64_t)b * 32;
-    const bool need_mask = (kt0 + 32 > Sk) || (CAUSAL && kt0 + 31 > qw0);
+    // mask: keys past Sk, keys above the diagonal. key = kt0 + kb*32 +
+    // 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or > this row's query:
+    // compare the compile-time part with a per-lane limit.
+    const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > qw0);
     if (need_mask) {
-      // key = kt0 + 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or above
-      // this row's diagonal: compare the compile-time part with a per-lane limit
       const int64_t kv = Sk - kt0;
-      int lim = kv < 32 ? (int)kv : 32;
+      int lim = kv < BN ? (int)kv : BN;
       if constexpr (CAUSAL) {
         const int64_t qr = qrow - kt0 + 1;
         lim = qr < lim ? (int)qr : lim;
       }
       lim -= 4 * hl;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sb[r] = (8 * (r >> 2) + (r & 3)) >= lim ? -INFINITY : sb[r];
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) >= lim ? -INFINITY : s[kb][r];
     }
+
+    // Online softmax (log2 domain). The running maximum of each row is kept
+    // exactly, so the largest P of a row is exactly 1; when it moves in some
+    // lane of the wave, O and l are rescaled by exp2(m_old - m_new).
     float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sb[r]);
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = wave_max_halves(mx);
     const float m_cand = fmaxf(m_run, mx * c);
-    rescale = __builtin_amdgcn_ballot_w64(m_cand > m_run) != 0;
-    if (rescale) {
-      const float m_use = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
-      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_cand;
-    }
-  }
-
-  // ---- apply a pending rescale of O and l ----
-  __device__ __forceinline__ void apply_rescale() {
-    if (rescale) {
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run) != 0) {
+      const float m_new = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
-      rescale = false;
+      m_run = m_cand;
     }
-  }
-
-  // ---- P_b = exp2(S_b * c - m) as the 16-bit P^T operand; l += sum P ----
-  __device__ __forceinline__ void softmax_p(const f32x16& sb) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+
+    u32x4 pf[NST];                     // P^T operand, one per 16-key step
+    u32x4 pl[SPLIT_P ? NST : 1];       // bf16 only: rounding residual of P
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      float pv[8];
+    for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
-      for (int r = 0; r < 8; ++r) pv[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sb[8 * half + r], c, -m_use));
-      u32x4 f;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        f[e] = pack2<KIND>(pv[2 * e], pv[2 * e + 1]);
-        l_run = add_pair<KIND>(f[e], l_run);     // l sums the P that multiplies V
-      }
-      pf[half] = f;
-      if constexpr (SPLIT_P) {
-        u32x4 g;
+      for (int half = 0; half < 2; ++half) {
+        u32x4 f, g;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          g[e] = pack2<KIND>(pv[2 * e] - unpack_lo<KIND>(f[e]), pv[2 * e + 1] - unpack_hi<KIND>(f[e]));
-          l_run = add_pair<KIND>(g[e], l_run);
+          const int r = 8 * half + 2 * e;
+          const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_use));
+          const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+          f[e] = pack2<KIND>(x0, x1);
+          l_run = add_pair<KIND>(f[e], l_run);     // l sums the P that multiplies V
+          if constexpr (SPLIT_P) {
+            g[e] = pack2<KIND>(x0 - unpack_lo<KIND>(f[e]), x1 - unpack_hi<KIND>(f[e]));
+            l_run = add_pair<KIND>(g[e], l_run);
+          }
         }
-        pl[half] = g;
+        pf[kb * 2 + half] = f;
+        if constexpr (SPLIT_P) pl[kb * 2 + half] = g;
       }
     }
-  }
 
-  // One 32-key block b = 4u + K of the four-block loop body (K compile-time):
-  // S_{b+1} and softmax(S_b); O += V_b^T P_b^T and mask/max of S_{b+1};
-  // then the stage hand-off.
-  template <int K>
-  __device__ __forceinline__ void block_step(int b, f32x16& s_cur, f32x16& s_nxt, bool& issued_prev) {
-    constexpr int OFF_CUR = (K >> 1) * TILE + (K & 1) * BLK;            // block b in its stage buffer
-    constexpr int OFF_NXT = (((K + 1) >> 1) & 1) * TILE + ((K + 1) & 1) * BLK;
-    apply_rescale();
-    if (b + 1 <= blast) gemm_s<OFF_NXT>(s_nxt);
-    if (b <= blast) softmax_p(s_cur);
-    if (b <= blast) gemm_pv<OFF_CUR>();
-    if (b + 1 <= blast) mask_max(s_nxt, b + 1);
-
-    // Stage t = b / 2 lives in buffer t % 2. Its K rows are last read in
-    // iteration 2t (S_{2t+1}), its V rows in iteration 2t+1 (PV_{2t+1}).
-    // After the barrier that ends iteration 2t the K of stage t+2 is
-    // loaded, after the one that ends 2t+1 its V; each batch is waited for
-    // at the end of the iteration after next, before the barrier that
-    // precedes its first reader (S_{2t+4} in iteration 2t+3, PV_{2t+4} in
-    // iteration 2t+4).
-    if (issued_prev) wait_loads<LOADS>(); else wait_loads<0>();
-    lds_barrier();
-    const int t = b >> 1;
-    issued_prev = false;
-    if (t + 2 < T) {
-      if constexpr ((K & 1) == 0) load_stage<false>(t + 2, K >> 1);
-      else load_stage<true>(t + 2, K >> 1);
-      issued_prev = true;
+    // O^T += V^T P^T; the V fragments of step st+1 are read while the MFMAs
+    // of step st run.
+    const uint32_t voff = buf * TILE;
+    u32x4 vf[2][NDB];
+    auto read_v = [&](int st, u32x4 (&dst)[NDB]) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        u32x2 y[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const fp16x4_tr x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+              (__attribute__((address_space(3))) fp16x4_tr*)(uintptr_t)(vaddr[db][e] + voff + st * 16 * C * 16));
+          __builtin_memcpy(&y[e], &x, 8);
+        }
+        dst[db] = (u32x4){y[0][0], y[0][1], y[1][0], y[1][1]};
+      }
+    };
+    read_v(0, vf[0]);
+#pragma unroll
+    for (int st = 0; st < NST; ++st) {
+      if (st + 1 < NST) read_v(st + 1, vf[(st + 1) & 1]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        acc_o[db] = mfma32<KIND>(vf[st & 1][db], pf[st], acc_o[db]);
+        if constexpr (SPLIT_P) acc_o[db] = mfma32<KIND>(vf[st & 1][db], pl[st], acc_o[db]);
+      }
     }
   }
 
   __device__ __forceinline__ void run() {
-    load_stage<false>(0, 0);
-    load_stage<true>(0, 0);
-    if (T > 1) {
-      load_stage<false>(1, 1);
-      load_stage<true>(1, 1);
-    }
-    wait_loads<0>();
-    lds_barrier();
-
-    f32x16 s0, s1;
-    if (blast >= 0) {
-      gemm_s<0>(s0);
-      mask_max(s0, 0);
-    }
-    bool issued_prev = false;
-    for (int b0 = 0; b0 < NB; b0 += 4) {
-      block_step<0>(b0, s0, s1, issued_prev);
-      if (b0 + 1 >= NB) break;
-      block_step<1>(b0 + 1, s1, s0, issued_prev);
-      if (b0 + 2 >= NB) break;
-      block_step<2>(b0 + 2, s0, s1, issued_prev);
-      if (b0 + 3 >= NB) break;
-      block_step<3>(b0 + 3, s1, s0, issued_prev);
+    load_tile(0, 0);
+    for (int j = 0; j < ntiles; ++j) {
+      const int buf = j & 1;
+      wait_loads();
+      lds_barrier();
+      if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
+      // Causal: a wave whose rows all lie above this tile's first key has
+      // nothing to add (all its scores here are masked).
+      if (CAUSAL && (int64_t)j * BN > qw0 + 31) continue;
+      tile(j, buf);
     }
     store();
   }
@@ -568,9 +518,12 @@ struct FwdBlock {
   }
 };
 
+// 32-key tiles: K and V double buffers take 4 x 32 x D x 2 bytes (32 KiB at
+// D = 128), so three workgroups (three waves per SIMD) fit in the 160 KiB
+// of LDS of a CU, and the register budget is capped to match.
 template <int D, bool CAUSAL, int KIND, int OUT>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(Params p) {
-  using Blk = FwdBlock<D, CAUSAL, KIND, OUT>;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void fa_fwd_kernel(Params p) {
+  using Blk = FwdTile<D, 32, CAUSAL, KIND, OUT>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
