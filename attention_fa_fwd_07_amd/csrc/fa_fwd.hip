@@ -40,6 +40,7 @@
 #include <stdint.h>
 #include <math.h>
 #include <float.h>
+#include <type_traits>
 
 #include "fa_mi355x.h"
 
@@ -146,19 +147,25 @@ __device__ __forceinline__ float unpack_hi(uint32_t x) {
   }
 }
 
-// XOR swizzles of the 16-byte chunks of one LDS row (row r, chunk c is stored
-// at chunk c ^ swz(r)). They depend on the head dim because the row pitch in
-// bytes does: the K swizzle spreads the 16 rows that one ds_read_b128 phase
-// touches over all 64 banks; the V swizzle spreads the four rows that one
-// transposing read touches over four different 64-byte bank groups.
-template <int D>
+// XOR swizzles of the 16-byte chunks of one LDS row (row r, chunk c is
+// stored at chunk c ^ swz(r)). They depend on the row pitch in bytes (RB:
+// 256 for 16-bit data at D=128, 128 for 16-bit at D=64 or fp8 at D=128, 64
+// for fp8 at D=64), because the pitch decides which rows share LDS banks.
+// The K swizzle spreads the 16 rows that one ds_read_b128 phase touches over
+// all 64 banks. The V swizzle for 16-bit data spreads the four rows that one
+// transposing read (ds_read_b64_tr_b16) touches over four different 64-byte
+// bank groups; fp8 V (ds_read_b64_tr_b8) uses the K pattern. Every swizzle
+// depends on the row index mod 16 only.
+template <int RB>
 __device__ __forceinline__ int swz_k(int r) {
-  if constexpr (D == 128) return r & 15;
-  else return (r >> 1) & 7;
+  if constexpr (RB == 256) return r & 15;
+  else if constexpr (RB == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
 }
-template <int D>
+template <int RB, bool TR8>
 __device__ __forceinline__ int swz_v(int r) {
-  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  if constexpr (TR8) return swz_k<RB>(r);
+  else if constexpr (RB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return ((r >> 1) & 1) << 2;
 }
 
@@ -224,29 +231,46 @@ __device__ __forceinline__ T lds_load(uint32_t addr) {
   return *(const __attribute__((address_space(3))) T*)(uintptr_t)addr;
 }
 
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 // One workgroup: 4 waves (256 lanes), BM = 128 query rows, 32 per wave.
-// Keys and values stream through LDS in tiles of BN = 64 rows, double
-// buffered: the loads of tile j+1 are issued right after the barrier that
-// opens tile j and waited for before the barrier that opens tile j+1. Per
-// tile each wave runs S^T = K Q^T (2 x D/16 MFMAs), the mask, the online
-// softmax and O^T += V^T P^T (4 x D/32 MFMAs); two waves share each SIMD,
-// so one wave's matrix products overlap the other's softmax.
+// Keys and values stream through LDS in tiles of BN rows, double buffered:
+// the loads of tile j+1 are issued right after the barrier that opens tile
+// j and waited for before the barrier that opens tile j+1. Per tile each
+// wave runs S^T = K Q^T, the mask, the online softmax and O^T += V^T P^T;
+// several waves share each SIMD, so one wave's matrix products overlap
+// another's softmax.
+//
+// fp8 (e4m3fn) inputs: S^T = K Q^T runs on v_mfma_scale_f32_32x32x64_f8f6f4
+// on the codes (unit block scales); the per-tensor descales of Q and K are
+// folded into the softmax scale. O^T += V^T P^T runs in fp16: P is fp16 as
+// for fp16 inputs, and the V codes, read transposed from LDS with
+// ds_read_b64_tr_b8, are converted exactly to fp16 (every e4m3fn value is
+// an fp16 value); the descale of V multiplies O in the epilogue.
 template <int D, int BN_, bool CAUSAL, int KIND, int OUT>
 struct FwdTile {
+  static constexpr bool F8 = (KIND == KFP8);
+  static constexpr int MK = F8 ? KF16 : KIND;     // type of the P.V product
   static constexpr int BN = BN_;                  // keys per tile
   static constexpr int BM = 128;                  // query rows per workgroup
   static constexpr int NT = 256;                  // lanes per workgroup
-  static constexpr int C = D / 8;                 // 16-byte chunks per K/V row
-  static constexpr int TILE = BN * D * 2;         // bytes of one K or V tile buffer
-  static constexpr int NDS = D / 16;              // k-steps of S = K Q^T
+  static constexpr int ES = F8 ? 1 : 2;           // bytes per input element
+  static constexpr int RB = D * ES;               // bytes per K/V row
+  static constexpr int C = RB / 16;               // 16-byte chunks per K/V row
+  static constexpr int TILE = BN * RB;            // bytes of one K or V tile buffer
+  static constexpr int NDS = F8 ? D / 64 : D / 16;  // k-steps of S = K Q^T
   static constexpr int NKB = BN / 32;             // 32-key blocks per tile
   static constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O
   static constexpr int NST = BN / 16;             // 16-key steps of O += V^T P^T
-  static constexpr int LOADS = BN * C / NT;       // 16-byte loads per lane, tile and tensor
+  static constexpr int NCH = BN * C;              // 16-byte chunks per tile
+  static constexpr int LOADS = NCH >= NT ? NCH / NT : 1;   // loads per lane, tile and tensor
+  static constexpr int LWAVES = NCH >= NT ? 4 : NCH / 64;  // waves that issue loads
   static constexpr bool SPLIT_P = (KIND == KBF16);  // bf16: P = hi + lo
   static constexpr int SMEM = 4 * TILE;           // K0 K1 V0 V1
-  static_assert(LOADS >= 1 && LOADS * NT == BN * C, "tile must split evenly over the lanes");
+  static_assert(NCH % 64 == 0 && (NCH >= NT ? NCH % NT == 0 : true), "tile must split evenly over the lanes");
   static_assert((NT / C) % 16 == 0, "swizzle period must divide the rows per load");
+
+  typedef typename std::conditional<F8, i32x8, u32x4>::type qfrag_t;
 
   const Params& p;
   uint32_t lds0;                    // LDS byte address of the tile buffers
@@ -255,11 +279,11 @@ struct FwdTile {
   int64_t Sq, Sk, q0, qw0, qrow;
   const char* khead;
   const char* vhead;
-  float c;
+  float c;                          // softmax scale in log2 units (fp8: times dq * dk)
 
-  u32x4 qf[NDS];
+  qfrag_t qf[NDS];
   uint32_t kaddr[NDS];              // K fragment addresses (buffer 0, key block 0)
-  uint32_t vaddr[NDB][2];           // V transposing-read addresses (buffer 0, step 0)
+  uint32_t vaddr[NDB][F8 ? 1 : 2];  // V transposing-read addresses (buffer 0, step 0)
   uint32_t goff_k, goff_v;          // this lane's byte offsets in a full tile (first load)
   f32x16 acc_o[NDB];
   float m_run, l_run;
@@ -278,45 +302,70 @@ struct FwdTile {
     Sq = p.Sq;
     Sk = p.Sk;
     q0 = (int64_t)qb * BM;
-    khead = p.k + (int64_t)bh * Sk * D * 2;
-    vhead = p.v + (int64_t)bh * Sk * D * 2;
+    khead = p.k + (int64_t)bh * Sk * RB;
+    vhead = p.v + (int64_t)bh * Sk * RB;
     qw0 = q0 + wave * 32;
     qrow = qw0 + l32;
     c = p.scale_log2;
+    if constexpr (F8) c = fmaxf(c * (*p.descale_q) * (*p.descale_k), FLT_MIN);
 
     int64_t kend = Sk;
     if constexpr (CAUSAL) kend = (q0 + BM) < Sk ? (q0 + BM) : Sk;
     ntiles = (int)((kend + BN - 1) / BN);
 
     // Q fragments (B operand of S^T = K Q^T), kept in registers; rows past
-    // Sq read the last row (their results are never stored)
-    const char* qhead = p.q + (int64_t)bh * Sq * D * 2;
-    const int64_t qrow_ld = qrow < Sq ? qrow : Sq - 1;
+    // Sq read the last row (their results are never stored). Negative
+    // scales negate Q (exact).
+    const char* qrowp = p.q + ((int64_t)bh * Sq + (qrow < Sq ? qrow : Sq - 1)) * RB;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
-      qf[ds] = *(const u32x4*)(qhead + (qrow_ld * D + ds * 16 + hl * 8) * 2);
-      if (p.negate) qf[ds] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      if constexpr (F8) {
+        // 32 consecutive codes: d = 64*ds + 32*hl .. +32
+        const u32x4 a = *(const u32x4*)(qrowp + 64 * ds + 32 * hl);
+        const u32x4 b = *(const u32x4*)(qrowp + 64 * ds + 32 * hl + 16);
+        const uint32_t sg = p.negate ? 0x80808080u : 0u;
+        qf[ds] = (i32x8){(int)(a[0] ^ sg), (int)(a[1] ^ sg), (int)(a[2] ^ sg), (int)(a[3] ^ sg),
+                         (int)(b[0] ^ sg), (int)(b[1] ^ sg), (int)(b[2] ^ sg), (int)(b[3] ^ sg)};
+      } else {
+        qf[ds] = *(const u32x4*)(qrowp + (ds * 16 + hl * 8) * 2);
+        if (p.negate) qf[ds] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      }
     }
 
-    // K (ds_read_b128): row l32 of a 32-key block, logical chunk 2*ds + hl,
-    // stored at chunk (2*ds + hl) ^ swz_k(row).
+    // K (ds_read_b128): row l32 of a 32-key block. 16-bit: logical chunk
+    // 2*ds + hl; fp8: chunks 4*ds + 2*hl and the next one (32 codes).
+    // Chunk c of row r is stored at chunk c ^ swz_k(r).
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds)
-      kaddr[ds] = lds0 + l32 * C * 16 + (((2 * ds + hl) ^ swz_k<D>(l32)) << 4);
-    // V (ds_read_b64_tr_b16): within each 16-lane group, lane i supplies row
-    // 16*step + 4*hl + (i/4) [+8 for the second read] and head-dim columns
-    // 32*db + 16*((lane/16)&1) + 4*(i%4) .. +4; the read returns to lane i the
-    // four keys of its head-dim column. The swizzle of a row only depends on
-    // its index mod 16, so one address per (db, read) serves every step.
+    for (int ds = 0; ds < NDS; ++ds) {
+      const int ch = F8 ? 4 * ds + 2 * hl : 2 * ds + hl;
+      kaddr[ds] = lds0 + l32 * RB + ((ch ^ swz_k<RB>(l32)) << 4);
+    }
+    // V, 16-bit (ds_read_b64_tr_b16): within each 16-lane group, lane i
+    // supplies row 16*step + 4*hl + (i/4) [+8 for the second read] and
+    // head-dim columns 32*db + 16*((lane/16)&1) + 4*(i%4) .. +4; the read
+    // returns to lane i the four keys of its head-dim column.
+    // V, fp8 (ds_read_b64_tr_b8): lane i supplies row 16*step +
+    // 8*((i/2)/4) + 4*hl + (i/2)%4 and columns 32*db + 16*((lane/16)&1) +
+    // 8*(i%2) .. +8; the read returns to lane i the eight keys of its column.
+    // Both key orders match the accumulator layout of S^T. The swizzle of
+    // a row only depends on its index mod 16, so one address per (db, read)
+    // serves every step.
     const int gi = lane & 15;
-    const int vcol = 16 * ((lane >> 4) & 1) + 4 * (gi & 3);
+    const int dh = (lane >> 4) & 1;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
+      if constexpr (F8) {
+        const int j = gi >> 1;
+        const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
+        const int ch = 2 * db + dh;
+        vaddr[db][0] = lds0 + 2 * TILE + r * RB + ((ch ^ swz_v<RB, true>(r)) << 4) + 8 * (gi & 1);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int r = 4 * hl + (gi >> 2) + 8 * e;
-        const int col = 32 * db + vcol;
-        vaddr[db][e] = lds0 + 2 * TILE + (r * C + ((col >> 3) ^ swz_v<D>(r))) * 16 + (col & 7) * 2;
+        for (int e = 0; e < 2; ++e) {
+          const int r = 4 * hl + (gi >> 2) + 8 * e;
+          const int col = 32 * db + 16 * dh + 4 * (gi & 3);
+          vaddr[db][e] = lds0 + 2 * TILE + r * RB + (((col >> 3) ^ swz_v<RB, false>(r)) << 4) + (col & 7) * 2;
+        }
       }
     }
     // HBM->LDS: lane chunk i*NT + tid of a tile; one wave writes a
@@ -327,8 +376,8 @@ struct FwdTile {
     {
       const int r = tid / C;
       const int pc = tid % C;
-      goff_k = (uint32_t)((r * D + (pc ^ swz_k<D>(r)) * 8) * 2);
-      goff_v = (uint32_t)((r * D + (pc ^ swz_v<D>(r)) * 8) * 2);
+      goff_k = (uint32_t)(r * RB + ((pc ^ swz_k<RB>(r)) << 4));
+      goff_v = (uint32_t)(r * RB + ((pc ^ swz_v<RB, F8>(r)) << 4));
     }
 
 #pragma unroll
@@ -340,17 +389,18 @@ struct FwdTile {
   // ---- HBM -> LDS: tile j of K and V into buffer buf ----
   // Rows past Sk read the last row (only the final tile can have them).
   __device__ __forceinline__ void load_tile(int j, int buf) {
+    if (wave >= LWAVES) return;
     const int64_t row0 = (int64_t)j * BN;
-    const char* kb = khead + row0 * (D * 2);
-    const char* vb = vhead + row0 * (D * 2);
+    const char* kb = khead + row0 * RB;
+    const char* vb = vhead + row0 * RB;
     const uint32_t kd = lds0 + buf * TILE + wave * 64 * 16;
     const uint32_t vd = lds0 + (2 + buf) * TILE + wave * 64 * 16;
     const int64_t left = Sk - 1 - row0;
     if (left >= BN - 1) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
-        dma16(kb + i * (NT / C) * D * 2, goff_k, kd + i * NT * 16);
-        dma16(vb + i * (NT / C) * D * 2, goff_v, vd + i * NT * 16);
+        dma16(kb + i * (NT / C) * RB, goff_k, kd + i * NT * 16);
+        dma16(vb + i * (NT / C) * RB, goff_v, vd + i * NT * 16);
       }
     } else {
       const int rmax = (int)left;
@@ -360,9 +410,37 @@ struct FwdTile {
         const int r = pidx / C;
         const int pc = pidx % C;
         const int rr = r < rmax ? r : rmax;
-        dma16(kb, (uint32_t)((rr * D + (pc ^ swz_k<D>(r)) * 8) * 2), kd + i * NT * 16);
-        dma16(vb, (uint32_t)((rr * D + (pc ^ swz_v<D>(r)) * 8) * 2), vd + i * NT * 16);
+        dma16(kb, (uint32_t)(rr * RB + ((pc ^ swz_k<RB>(r)) << 4)), kd + i * NT * 16);
+        dma16(vb, (uint32_t)(rr * RB + ((pc ^ swz_v<RB, F8>(r)) << 4)), vd + i * NT * 16);
       }
+    }
+  }
+
+  // V^T fragment (A operand of O^T += V^T P^T) of 16-key step st, head-dim block db
+  __device__ __forceinline__ u32x4 v_frag(uint32_t voff, int st, int db) {
+    if constexpr (F8) {
+      typedef int i32x2 __attribute__((ext_vector_type(2)));
+      const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (__attribute__((address_space(3))) i32x2*)(uintptr_t)(vaddr[db][0] + voff + st * 16 * RB));
+      // codes 0..3 of a dword hold keys 4w .. 4w+3 of this lane's column
+      uint32_t r[4];
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const half2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)x[w], 1.0f, false);
+        const half2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((uint32_t)x[w], 1.0f, true);
+        __builtin_memcpy(&r[2 * w], &lo, 4);
+        __builtin_memcpy(&r[2 * w + 1], &hi, 4);
+      }
+      return (u32x4){r[0], r[1], r[2], r[3]};
+    } else {
+      u32x2 y[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const fp16x4_tr x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+            (__attribute__((address_space(3))) fp16x4_tr*)(uintptr_t)(vaddr[db][e] + voff + st * 16 * RB));
+        __builtin_memcpy(&y[e], &x, 8);
+      }
+      return (u32x4){y[0][0], y[0][1], y[1][0], y[1][1]};
     }
   }
 
@@ -375,12 +453,25 @@ struct FwdTile {
     f32x16 s[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      u32x4 kf[NDS];
-#pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) kf[ds] = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * C * 16);
       s[kb] = (f32x16){};
+      if constexpr (F8) {
+        i32x8 kf[NDS];
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma32<KIND>(kf[ds], qf[ds], s[kb]);
+        for (int ds = 0; ds < NDS; ++ds) {
+          const u32x4 a = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
+          const u32x4 b = lds_load<u32x4>((kaddr[ds] ^ 16) + koff + kb * 32 * RB);
+          kf[ds] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        }
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[ds], qf[ds], s[kb], 0, 0, 0, 127, 0, 127);
+      } else {
+        u32x4 kf[NDS];
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) kf[ds] = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
+#pragma unroll
+        for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma32<KIND>(kf[ds], qf[ds], s[kb]);
+      }
     }
 
     // mask: keys past Sk, keys above the diagonal. key = kt0 + kb*32 +
@@ -433,11 +524,11 @@ struct FwdTile {
           const int r = 8 * half + 2 * e;
           const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_use));
           const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -m_use));
-          f[e] = pack2<KIND>(x0, x1);
-          l_run = add_pair<KIND>(f[e], l_run);     // l sums the P that multiplies V
+          f[e] = pack2<MK>(x0, x1);
+          l_run = add_pair<MK>(f[e], l_run);     // l sums the P that multiplies V
           if constexpr (SPLIT_P) {
-            g[e] = pack2<KIND>(x0 - unpack_lo<KIND>(f[e]), x1 - unpack_hi<KIND>(f[e]));
-            l_run = add_pair<KIND>(g[e], l_run);
+            g[e] = pack2<MK>(x0 - unpack_lo<MK>(f[e]), x1 - unpack_hi<MK>(f[e]));
+            l_run = add_pair<MK>(g[e], l_run);
           }
         }
         pf[kb * 2 + half] = f;
@@ -449,27 +540,18 @@ struct FwdTile {
     // of step st run.
     const uint32_t voff = buf * TILE;
     u32x4 vf[2][NDB];
-    auto read_v = [&](int st, u32x4 (&dst)[NDB]) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        u32x2 y[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const fp16x4_tr x = __builtin_amdgcn_ds_read_tr16_b64_v4f16(
-              (__attribute__((address_space(3))) fp16x4_tr*)(uintptr_t)(vaddr[db][e] + voff + st * 16 * C * 16));
-          __builtin_memcpy(&y[e], &x, 8);
-        }
-        dst[db] = (u32x4){y[0][0], y[0][1], y[1][0], y[1][1]};
-      }
-    };
-    read_v(0, vf[0]);
+    for (int db = 0; db < NDB; ++db) vf[0][db] = v_frag(voff, 0, db);
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
-      if (st + 1 < NST) read_v(st + 1, vf[(st + 1) & 1]);
+      if (st + 1 < NST) {
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) vf[(st + 1) & 1][db] = v_frag(voff, st + 1, db);
+      }
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        acc_o[db] = mfma32<KIND>(vf[st & 1][db], pf[st], acc_o[db]);
-        if constexpr (SPLIT_P) acc_o[db] = mfma32<KIND>(vf[st & 1][db], pl[st], acc_o[db]);
+        acc_o[db] = mfma32<MK>(vf[st & 1][db], pf[st], acc_o[db]);
+        if constexpr (SPLIT_P) acc_o[db] = mfma32<MK>(vf[st & 1][db], pl[st], acc_o[db]);
       }
     }
   }
@@ -489,10 +571,11 @@ struct FwdTile {
     store();
   }
 
-  // ---- epilogue: O = O / l, lse = (m + log2 l) * ln 2 ----
+  // ---- epilogue: O = O / l (fp8: times the V descale), lse = (m + log2 l) * ln 2 ----
   __device__ __forceinline__ void store() {
     const float l_tot = wave_sum_halves(l_run);
-    const float inv_l = 1.f / l_tot;
+    float inv_l = 1.f / l_tot;
+    if constexpr (F8) inv_l *= *p.descale_v;
     if (qrow >= Sq) return;
     char* orow = p.o + ((int64_t)bh * Sq + qrow) * D * (OUT == OF32 ? 4 : 2);
 #pragma unroll
@@ -605,7 +688,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (!ok_pair) return FA_ERR_UNSUPPORTED_DTYPE;
   if (in_dtype == FA_FP8_E4M3) {
     if (!descale_q || !descale_k || !descale_v) return FA_ERR_NULL_POINTER;
-    return FA_ERR_UNSUPPORTED_DTYPE;   // fp8 kernels are not built yet
+    if (((uintptr_t)descale_q | (uintptr_t)descale_k | (uintptr_t)descale_v) & 3) return FA_ERR_MISALIGNED;
   }
   if (layout != FA_LAYOUT_BNSD) return FA_ERR_UNSUPPORTED_LAYOUT;
   if (keep_prob != 1.0f) return FA_ERR_UNSUPPORTED_DROPOUT;
@@ -656,6 +739,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     fn = (o_dtype == FA_F32) ? pick_d<fa::KF16, fa::OF32>(D, cz) : pick_d<fa::KF16, fa::OF16>(D, cz);
   } else if (in_dtype == FA_BF16) {
     fn = (o_dtype == FA_F32) ? pick_d<fa::KBF16, fa::OF32>(D, cz) : pick_d<fa::KBF16, fa::OBF16>(D, cz);
+  } else if (in_dtype == FA_FP8_E4M3) {
+    fn = (o_dtype == FA_F32) ? pick_d<fa::KFP8, fa::OF32>(D, cz) : pick_d<fa::KFP8, fa::OF16>(D, cz);
   }
   if (!fn) return FA_ERR_UNSUPPORTED_DTYPE;
 

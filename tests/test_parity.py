@@ -21,7 +21,7 @@ LENGTHS = [(1, 1), (2, 2), (63, 63), (64, 64), (65, 65), (127, 127), (128, 128),
            (200, 1), (130, 513)]
 
 
-@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16])
+@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16, fi.FP8])
 @pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 def test_edge_sweep(dtype, D, causal):
@@ -35,11 +35,12 @@ def test_edge_sweep(dtype, D, causal):
             compare(cfg, od, o, lse, ref_o, ref_l, what=f"{dtype} D{D} c{causal} {Sq}x{Sk} {od}")
 
 
-def test_scale_variants():
+@pytest.mark.parametrize("dtype", [fi.F16, fi.FP8])
+def test_scale_variants(dtype):
     """Negative and zero scale (zero: uniform weights over the visible keys)."""
     for scale in (-0.3, 0.0, 2.0):
         for causal in (False, True):
-            cfg = fi.Config("scale", 1, 2, 77, 77, 64, fi.F16, causal, seed=9, scale=scale)
+            cfg = fi.Config("scale", 1, 2, 77, 77, 64, dtype, causal, seed=9, scale=scale)
             inp = fi.make_inputs(cfg)
             ref_o, ref_l = oracle_full(cfg, inp)
             o, lse = run_gpu(cfg, inp, fi.F32)
@@ -55,8 +56,6 @@ def _heads_to_check(cfg, rng):
 @pytest.mark.parametrize("idx", range(len(fi.CONFIGS)), ids=[c.name for c in fi.CONFIGS])
 def test_workload_full_size(idx):
     cfg = fi.CONFIGS[idx]
-    if cfg.dtype == fi.FP8:
-        pytest.skip("fp8 e4m3 kernels are not built yet")
     inp = fi.make_inputs(cfg)
     rng = np.random.default_rng(idx)
     whole, sampled = _heads_to_check(cfg, rng)
