@@ -445,9 +445,12 @@ struct FwdTile {
   }
 
   // ---- one tile: S, mask, online softmax, O += V^T P^T ----
-  __device__ __forceinline__ void tile(int j, int buf) {
+  // BUF is compile-time so that every LDS address is a per-lane base plus
+  // an immediate offset.
+  template <int BUF>
+  __device__ __forceinline__ void tile(int j) {
     const int64_t kt0 = (int64_t)j * BN;
-    const uint32_t koff = buf * TILE;
+    constexpr uint32_t koff = BUF * TILE;
 
     // S^T = K Q^T for NKB blocks of 32 keys
     f32x16 s[NKB];
@@ -538,7 +541,7 @@ struct FwdTile {
 
     // O^T += V^T P^T; the V fragments of step st+1 are read while the MFMAs
     // of step st run.
-    const uint32_t voff = buf * TILE;
+    constexpr uint32_t voff = BUF * TILE;
     u32x4 vf[2][NDB];
 #pragma unroll
     for (int db = 0; db < NDB; ++db) vf[0][db] = v_frag(voff, 0, db);
@@ -556,17 +559,23 @@ struct FwdTile {
     }
   }
 
+  template <int BUF>
+  __device__ __forceinline__ void step(int j) {
+    wait_loads();
+    lds_barrier();
+    if (j + 1 < ntiles) load_tile(j + 1, BUF ^ 1);
+    // Causal: a wave whose rows all lie above this tile's first key has
+    // nothing to add (all its scores here are masked).
+    if (CAUSAL && (int64_t)j * BN > qw0 + 31) return;
+    tile<BUF>(j);
+  }
+
   __device__ __forceinline__ void run() {
     load_tile(0, 0);
-    for (int j = 0; j < ntiles; ++j) {
-      const int buf = j & 1;
-      wait_loads();
-      lds_barrier();
-      if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
-      // Causal: a wave whose rows all lie above this tile's first key has
-      // nothing to add (all its scores here are masked).
-      if (CAUSAL && (int64_t)j * BN > qw0 + 31) continue;
-      tile(j, buf);
+    for (int j = 0; j < ntiles; j += 2) {   // tile j in buffer 0, j + 1 in buffer 1
+      step<0>(j);
+      if (j + 1 >= ntiles) break;
+      step<1>(j + 1);
     }
     store();
   }
