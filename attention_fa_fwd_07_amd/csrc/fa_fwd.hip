@@ -23,8 +23,8 @@
 //    product in registers (no LDS round trip), with the key order inside a
 //    16-key step chosen to match the accumulator layout.
 //  * K and V tiles go from HBM straight into LDS (global_load_lds, 16 bytes
-//    per lane), double buffered, in an XOR-swizzled layout chosen per head
-//    dim; K is read with ds_read_b128, V with the transposing
+//    per lane), through a ring of three buffers (two tiles in flight while
+//    one is computed on), in an XOR-swizzled layout chosen per head dim; K is read with ds_read_b128, V with the transposing
 //    ds_read_b64_tr_b16, which delivers V^T fragments directly.
 //  * Tail guards: rows past Sq or Sk are clamped to the last valid row, so
 //    every load reads mapped memory holding finite values; keys past Sk and
@@ -212,17 +212,20 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
 // (lgkmcnt) but not for its HBM->LDS loads, which are waited for explicitly
-// (wait_loads) one tile after they are issued. The scheduling fences keep
+// (wait_loads) before the tile that reads them. The scheduling fences keep
 // the compiler from moving instructions across it.
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
-// Wait until none of this wave's HBM->LDS loads is outstanding.
+// Wait until at most N of this wave's HBM->LDS loads are outstanding (they
+// complete in issue order).
+template <int N>
 __device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
   __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
   __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -234,9 +237,10 @@ __device__ __forceinline__ T lds_load(uint32_t addr) {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // One workgroup: 4 waves (256 lanes), BM = 128 query rows, 32 per wave.
-// Keys and values stream through LDS in tiles of BN rows, double buffered:
-// the loads of tile j+1 are issued right after the barrier that opens tile
-// j and waited for before the barrier that opens tile j+1. Per tile each
+// Keys and values stream through LDS in tiles of BN rows, in a ring of NB
+// buffers per tensor: the loads of tile j+NB-1 are issued right after the
+// barrier that opens tile j and waited for before the barrier that opens
+// tile j+NB-1, so they have NB-1 tiles of compute to arrive. Per tile each
 // wave runs S^T = K Q^T, the mask, the online softmax and O^T += V^T P^T;
 // several waves share each SIMD, so one wave's matrix products overlap
 // another's softmax.
@@ -247,13 +251,15 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // for fp16 inputs, and the V codes, read transposed from LDS with
 // ds_read_b64_tr_b8, are converted exactly to fp16 (every e4m3fn value is
 // an fp16 value); the descale of V multiplies O in the epilogue.
-template <int D, int BN_, bool CAUSAL, int KIND, int OUT>
+template <int D, int BN_, int NB_, bool CAUSAL, int KIND, int OUT>
 struct FwdTile {
   static constexpr bool F8 = (KIND == KFP8);
   static constexpr int MK = F8 ? KF16 : KIND;     // type of the P.V product
   static constexpr int BN = BN_;                  // keys per tile
-  static constexpr int BM = 128;                  // query rows per workgroup
-  static constexpr int NT = 256;                  // lanes per workgroup
+  static constexpr int NW = 4;                     // waves per workgroup
+  static constexpr int NB = NB_;                  // K/V tile buffers (ring)
+  static constexpr int BM = 32 * NW;              // query rows per workgroup
+  static constexpr int NT = 256;                  // lanes that issue the HBM->LDS loads
   static constexpr int ES = F8 ? 1 : 2;           // bytes per input element
   static constexpr int RB = D * ES;               // bytes per K/V row
   static constexpr int C = RB / 16;               // 16-byte chunks per K/V row
@@ -264,9 +270,10 @@ struct FwdTile {
   static constexpr int NST = BN / 16;             // 16-key steps of O += V^T P^T
   static constexpr int NCH = BN * C;              // 16-byte chunks per tile
   static constexpr int LOADS = NCH >= NT ? NCH / NT : 1;   // loads per lane, tile and tensor
-  static constexpr int LWAVES = NCH >= NT ? 4 : NCH / 64;  // waves that issue loads
+  static constexpr int LWAVES = NCH >= NT ? 4 : NCH / 64;  // waves that issue loads (of the first four)
   static constexpr bool SPLIT_P = (KIND == KBF16);  // bf16: P = hi + lo
-  static constexpr int SMEM = 4 * TILE;           // K0 K1 V0 V1
+  static constexpr int SMEM = 2 * NB * TILE;      // K ring, then V ring
+  static_assert(NB == 2 || NB == 3, "two or three buffers");
   static_assert(NCH % 64 == 0 && (NCH >= NT ? NCH % NT == 0 : true), "tile must split evenly over the lanes");
   static_assert((NT / C) % 16 == 0, "swizzle period must divide the rows per load");
 
@@ -275,7 +282,7 @@ struct FwdTile {
   const Params& p;
   uint32_t lds0;                    // LDS byte address of the tile buffers
   int tid, lane, wave, hl, l32;
-  int bh, ntiles;
+  int bh, ntiles, jlast;
   int64_t Sq, Sk, q0, qw0, qrow;
   const char* khead;
   const char* vhead;
@@ -312,6 +319,11 @@ struct FwdTile {
     int64_t kend = Sk;
     if constexpr (CAUSAL) kend = (q0 + BM) < Sk ? (q0 + BM) : Sk;
     ntiles = (int)((kend + BN - 1) / BN);
+    jlast = ntiles - 1;   // last tile this wave needs
+    if constexpr (CAUSAL) {
+      const int64_t jl = (qw0 + 31) / BN;
+      jlast = jl < jlast ? (int)jl : jlast;
+    }
 
     // Q fragments (B operand of S^T = K Q^T), kept in registers; rows past
     // Sq read the last row (their results are never stored). Negative
@@ -358,23 +370,23 @@ struct FwdTile {
         const int j = gi >> 1;
         const int r = 8 * (j >> 2) + 4 * hl + (j & 3);
         const int ch = 2 * db + dh;
-        vaddr[db][0] = lds0 + 2 * TILE + r * RB + ((ch ^ swz_v<RB, true>(r)) << 4) + 8 * (gi & 1);
+        vaddr[db][0] = lds0 + NB * TILE + r * RB + ((ch ^ swz_v<RB, true>(r)) << 4) + 8 * (gi & 1);
       } else {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
           const int r = 4 * hl + (gi >> 2) + 8 * e;
           const int col = 32 * db + 16 * dh + 4 * (gi & 3);
-          vaddr[db][e] = lds0 + 2 * TILE + r * RB + (((col >> 3) ^ swz_v<RB, false>(r)) << 4) + (col & 7) * 2;
+          vaddr[db][e] = lds0 + NB * TILE + r * RB + (((col >> 3) ^ swz_v<RB, false>(r)) << 4) + (col & 7) * 2;
         }
       }
     }
-    // HBM->LDS: lane chunk i*NT + tid of a tile; one wave writes a
-    // contiguous KiB of LDS per instruction, so the swizzle is applied to
-    // the global source offset. Load i covers rows r + i*NT/C; the swizzle
-    // only depends on the row mod 16, so every load of a lane uses the same
-    // chunk and the offsets differ by i*(NT/C) rows.
+    // HBM->LDS (lanes 0..255 only): lane chunk i*NT + tid of a tile; one
+    // wave writes a contiguous KiB of LDS per instruction, so the swizzle is
+    // applied to the global source offset. Load i covers rows r + i*NT/C;
+    // the swizzle only depends on the row mod 16, so every load of a lane
+    // uses the same chunk and the offsets differ by i*(NT/C) rows.
     {
-      const int r = tid / C;
+      const int r = (tid & (NT - 1)) / C;
       const int pc = tid % C;
       goff_k = (uint32_t)(r * RB + ((pc ^ swz_k<RB>(r)) << 4));
       goff_v = (uint32_t)(r * RB + ((pc ^ swz_v<RB, F8>(r)) << 4));
@@ -386,22 +398,19 @@ struct FwdTile {
     l_run = 0.f;
   }
 
-  // ---- HBM -> LDS: tile j of K and V into buffer buf ----
+  // ---- HBM -> LDS: tile j of K or V into buffer buf (lanes 0..255) ----
   // Rows past Sk read the last row (only the final tile can have them).
-  __device__ __forceinline__ void load_tile(int j, int buf) {
-    if (wave >= LWAVES) return;
+  template <bool IS_V>
+  __device__ __forceinline__ void load_one(int j, int buf) {
+    if (wave >= LWAVES) return;   // only the first LWAVES waves issue loads
     const int64_t row0 = (int64_t)j * BN;
-    const char* kb = khead + row0 * RB;
-    const char* vb = vhead + row0 * RB;
-    const uint32_t kd = lds0 + buf * TILE + wave * 64 * 16;
-    const uint32_t vd = lds0 + (2 + buf) * TILE + wave * 64 * 16;
+    const char* base = (IS_V ? vhead : khead) + row0 * RB;
+    const uint32_t dst = lds0 + (IS_V ? NB + buf : buf) * TILE + wave * 64 * 16;
+    const uint32_t goff = IS_V ? goff_v : goff_k;
     const int64_t left = Sk - 1 - row0;
     if (left >= BN - 1) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        dma16(kb + i * (NT / C) * RB, goff_k, kd + i * NT * 16);
-        dma16(vb + i * (NT / C) * RB, goff_v, vd + i * NT * 16);
-      }
+      for (int i = 0; i < LOADS; ++i) dma16(base + i * (NT / C) * RB, goff, dst + i * NT * 16);
     } else {
       const int rmax = (int)left;
 #pragma unroll
@@ -410,10 +419,14 @@ struct FwdTile {
         const int r = pidx / C;
         const int pc = pidx % C;
         const int rr = r < rmax ? r : rmax;
-        dma16(kb, (uint32_t)(rr * RB + ((pc ^ swz_k<RB>(r)) << 4)), kd + i * NT * 16);
-        dma16(vb, (uint32_t)(rr * RB + ((pc ^ swz_v<RB, F8>(r)) << 4)), vd + i * NT * 16);
+        const int sw = IS_V ? swz_v<RB, F8>(r) : swz_k<RB>(r);
+        dma16(base, (uint32_t)(rr * RB + ((pc ^ sw) << 4)), dst + i * NT * 16);
       }
     }
+  }
+  __device__ __forceinline__ void load_tile(int j, int buf) {
+    load_one<false>(j, buf);
+    load_one<true>(j, buf);
   }
 
   // V^T fragment (A operand of O^T += V^T P^T) of 16-key step st, head-dim block db
@@ -444,44 +457,75 @@ struct FwdTile {
     }
   }
 
-  // ---- one tile: S, mask, online softmax, O += V^T P^T ----
-  // BUF is compile-time so that every LDS address is a per-lane base plus
-  // an immediate offset.
-  template <int BUF>
-  __device__ __forceinline__ void tile(int j) {
-    const int64_t kt0 = (int64_t)j * BN;
-    constexpr uint32_t koff = BUF * TILE;
+  // ---- S^T = K Q^T for one tile (buffer BUF) ----
+  // The K fragments are read first (read_k) and the MFMA chain runs once
+  // they are in registers (mma_s), so the LDS latency is paid once per
+  // tile instead of once per MFMA.
+  typedef typename std::conditional<F8, i32x8, u32x4>::type kfrag_t;
 
-    // S^T = K Q^T for NKB blocks of 32 keys
-    f32x16 s[NKB];
+  template <int BUF>
+  __device__ __forceinline__ void read_k(kfrag_t (&kf)[NKB][NDS]) {
+    constexpr uint32_t koff = BUF * TILE;
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int ds = 0; ds < NDS; ++ds) {
+        if constexpr (F8) {
+          const u32x4 a = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
+          const u32x4 b = lds_load<u32x4>((kaddr[ds] ^ 16) + koff + kb * 32 * RB);
+          kf[kb][ds] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+        } else {
+          kf[kb][ds] = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
+        }
+      }
+    }
+  }
+
+  __device__ __forceinline__ void mma_s(const kfrag_t (&kf)[NKB][NDS], f32x16 (&s)[NKB]) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = (f32x16){};
-      if constexpr (F8) {
-        i32x8 kf[NDS];
 #pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) {
-          const u32x4 a = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
-          const u32x4 b = lds_load<u32x4>((kaddr[ds] ^ 16) + koff + kb * 32 * RB);
-          kf[ds] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
-        }
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds)
-          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[ds], qf[ds], s[kb], 0, 0, 0, 127, 0, 127);
-      } else {
-        u32x4 kf[NDS];
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) kf[ds] = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
-#pragma unroll
-        for (int ds = 0; ds < NDS; ++ds) s[kb] = mfma32<KIND>(kf[ds], qf[ds], s[kb]);
+      for (int ds = 0; ds < NDS; ++ds) {
+        if constexpr (F8)
+          s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[kb][ds], qf[ds], s[kb], 0, 0, 0, 127, 0, 127);
+        else
+          s[kb] = mfma32<KIND>(kf[kb][ds], qf[ds], s[kb]);
       }
     }
+  }
 
+  template <int BUF>
+  __device__ __forceinline__ void gemm_s(f32x16 (&s)[NKB]) {
+    kfrag_t kf[NKB][NDS];
+    read_k<BUF>(kf);
+    mma_s(kf, s);
+#ifndef KPIPE
+#define KPIPE 4
+#endif
+    if constexpr (!F8 && NKB == 1 && NDS > KPIPE) {
+      // KPIPE reads in flight ahead of the MFMA that consumes them.
+      __builtin_amdgcn_sched_group_barrier(0x100, KPIPE, 0);
+#pragma unroll
+      for (int i = 0; i < NDS - KPIPE; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, KPIPE, 0);
+    }
+  }
+
+  // ---- mask, online softmax and P for tile j ----
+  __device__ __forceinline__ void softmax(int j, f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1]) {
+    const int64_t kt0 = (int64_t)j * BN;
     // mask: keys past Sk, keys above the diagonal. key = kt0 + kb*32 +
     // 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or > this row's query:
     // compare the compile-time part with a per-lane limit.
     const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > qw0);
     if (need_mask) {
+      // keeps this a branch: full tiles (all but the last, or the diagonal
+      // ones) then skip the compare-and-select on every score
+      asm volatile("");
       const int64_t kv = Sk - kt0;
       int lim = kv < BN ? (int)kv : BN;
       if constexpr (CAUSAL) {
@@ -495,9 +539,15 @@ struct FwdTile {
         for (int r = 0; r < 16; ++r) s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) >= lim ? -INFINITY : s[kb][r];
     }
 
-    // Online softmax (log2 domain). The running maximum of each row is kept
-    // exactly, so the largest P of a row is exactly 1; when it moves in some
-    // lane of the wave, O and l are rescaled by exp2(m_old - m_new).
+    // Online softmax (log2 domain) with a reference maximum m_run: P =
+    // exp2(S*c - m_run), O and l accumulate relative to it, and moving it
+    // rescales O and l by exp2(m_old - m_new). While a row has few
+    // effective keys (l < 2^6 in units of its largest P) the reference
+    // follows the running maximum exactly, so the largest P is exactly 1 and
+    // carries no fp16 rounding error. Once l is large, a new maximum within
+    // log2(l) - 6 (at most 8) of the reference keeps the reference: that P is
+    // at most l / 64, so its rounding error weighs at most 2^-17 of O, and
+    // most tiles of long rows skip the rescale.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -505,7 +555,10 @@ struct FwdTile {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = wave_max_halves(mx);
     const float m_cand = fmaxf(m_run, mx * c);
-    if (__builtin_amdgcn_ballot_w64(m_cand > m_run) != 0) {
+    // slack in log2 units: clamp(log2(l) - 6, 0, 8); l of this lane's half
+    // of the keys bounds the row's l from below
+    const float slack = __builtin_amdgcn_fmed3f(__builtin_amdgcn_logf(l_run) - 6.0f, 0.0f, 8.0f);
+    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + slack) != 0) {
       const float m_new = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
@@ -515,8 +568,6 @@ struct FwdTile {
     }
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 
-    u32x4 pf[NST];                     // P^T operand, one per 16-key step
-    u32x4 pl[SPLIT_P ? NST : 1];       // bf16 only: rounding residual of P
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -538,9 +589,12 @@ struct FwdTile {
         if constexpr (SPLIT_P) pl[kb * 2 + half] = g;
       }
     }
+  }
 
-    // O^T += V^T P^T; the V fragments of step st+1 are read while the MFMAs
-    // of step st run.
+  // ---- O^T += V^T P^T for one tile (buffer BUF); the V fragments of step
+  // st+1 are read while the MFMAs of step st run ----
+  template <int BUF>
+  __device__ __forceinline__ void gemm_pv(const u32x4 (&pf)[NST], const u32x4 (&pl)[SPLIT_P ? NST : 1]) {
     constexpr uint32_t voff = BUF * TILE;
     u32x4 vf[2][NDB];
 #pragma unroll
@@ -559,23 +613,46 @@ struct FwdTile {
     }
   }
 
+  // ---- one tile: S, mask, online softmax, O += V^T P^T ----
+  template <int BUF>
+  __device__ __forceinline__ void tile(int j) {
+    f32x16 s[NKB];
+    u32x4 pf[NST];
+    u32x4 pl[SPLIT_P ? NST : 1];
+    gemm_s<BUF>(s);
+    softmax(j, s, pf, pl);
+    gemm_pv<BUF>(pf, pl);
+  }
+
   template <int BUF>
   __device__ __forceinline__ void step(int j) {
-    wait_loads();
+    // this wave's part of tile j has landed once at most the loads of the
+    // younger tiles in flight (j+1 .. j+NB-2) are outstanding; the barrier
+    // then makes the whole tile visible and frees buffer (j-1) % NB, last
+    // read while computing tile j-1
+    if (j + NB - 2 < ntiles) wait_loads<(NB - 2) * 2 * LOADS>();
+    else wait_loads<0>();
     lds_barrier();
-    if (j + 1 < ntiles) load_tile(j + 1, BUF ^ 1);
+    if (j + NB - 1 < ntiles) load_tile(j + NB - 1, (BUF + NB - 1) % NB);
     // Causal: a wave whose rows all lie above this tile's first key has
     // nothing to add (all its scores here are masked).
-    if (CAUSAL && (int64_t)j * BN > qw0 + 31) return;
+    if (j > jlast) return;
     tile<BUF>(j);
   }
 
   __device__ __forceinline__ void run() {
-    load_tile(0, 0);
-    for (int j = 0; j < ntiles; j += 2) {   // tile j in buffer 0, j + 1 in buffer 1
+    // tile j lives in buffer j % NB; tiles j+1 .. j+NB-1 are in flight
+#pragma unroll
+    for (int i = 0; i < NB - 1; ++i)
+      if (i < ntiles) load_tile(i, i);
+    for (int j = 0; j < ntiles; j += NB) {
       step<0>(j);
       if (j + 1 >= ntiles) break;
       step<1>(j + 1);
+      if constexpr (NB == 3) {
+        if (j + 2 >= ntiles) break;
+        step<2>(j + 2);
+      }
     }
     store();
   }
@@ -610,12 +687,16 @@ struct FwdTile {
   }
 };
 
-// 32-key tiles: K and V double buffers take 4 x 32 x D x 2 bytes (32 KiB at
-// D = 128), so three workgroups (three waves per SIMD) fit in the 160 KiB
-// of LDS of a CU, and the register budget is capped to match.
+// 32-key tiles in a ring of FA_NBUF buffers per tensor: 2 x 3 x 32 x D x 2
+// bytes (48 KiB at D = 128), so three 4-wave workgroups (three waves per
+// SIMD) fit in the 160 KiB of LDS of a CU, and the register budget is
+// capped to match.
+#ifndef FA_NBUF
+#define FA_NBUF 3
+#endif
 template <int D, bool CAUSAL, int KIND, int OUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void fa_fwd_kernel(Params p) {
-  using Blk = FwdTile<D, 32, CAUSAL, KIND, OUT>;
+  using Blk = FwdTile<D, 32, FA_NBUF, CAUSAL, KIND, OUT>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
@@ -709,7 +790,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (B > lim / H || Sq > lim || Sk > lim) return FA_ERR_BAD_SHAPE;
   const int64_t BH = B * H;
   if (BH > (lim / Sq) || BH > (lim / Sk)) return FA_ERR_BAD_SHAPE;
-  const int64_t nqb = (Sq + 127) / 128;
+  const int64_t nqb = (Sq + 127) / 128;   // 128 query rows per workgroup
   if (nqb > INT32_MAX || BH * nqb > INT32_MAX) return FA_ERR_BAD_SHAPE;
 
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
