@@ -236,7 +236,7 @@ __device__ __forceinline__ T lds_load(uint32_t addr) {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// One workgroup: 4 waves (256 lanes), BM = 128 query rows, 32 per wave.
+// One workgroup: NW waves, BM = 32 * NW query rows, 32 per wave.
 // Keys and values stream through LDS in tiles of BN rows, in a ring of NB
 // buffers per tensor: the loads of tile j+NB-1 are issued right after the
 // barrier that opens tile j and waited for before the barrier that opens
@@ -251,15 +251,14 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // for fp16 inputs, and the V codes, read transposed from LDS with
 // ds_read_b64_tr_b8, are converted exactly to fp16 (every e4m3fn value is
 // an fp16 value); the descale of V multiplies O in the epilogue.
-template <int D, int BN_, int NB_, bool CAUSAL, int KIND, int OUT>
+template <int D, int BN_, int NW_, int NB_, bool CAUSAL, int KIND, int OUT>
 struct FwdTile {
   static constexpr bool F8 = (KIND == KFP8);
   static constexpr int MK = F8 ? KF16 : KIND;     // type of the P.V product
   static constexpr int BN = BN_;                  // keys per tile
-  static constexpr int NW = 4;                     // waves per workgroup
+  static constexpr int NW = NW_;                  // waves per workgroup
   static constexpr int NB = NB_;                  // K/V tile buffers (ring)
   static constexpr int BM = 32 * NW;              // query rows per workgroup
-  static constexpr int NT = 256;                  // lanes that issue the HBM->LDS loads
   static constexpr int ES = F8 ? 1 : 2;           // bytes per input element
   static constexpr int RB = D * ES;               // bytes per K/V row
   static constexpr int C = RB / 16;               // 16-byte chunks per K/V row
@@ -269,12 +268,13 @@ struct FwdTile {
   static constexpr int NDB = D / 32;              // 32-wide head-dim blocks of O
   static constexpr int NST = BN / 16;             // 16-key steps of O += V^T P^T
   static constexpr int NCH = BN * C;              // 16-byte chunks per tile
-  static constexpr int LOADS = NCH >= NT ? NCH / NT : 1;   // loads per lane, tile and tensor
-  static constexpr int LWAVES = NCH >= NT ? 4 : NCH / 64;  // waves that issue loads (of the first four)
+  static constexpr int LWAVES = NCH / 64 < NW ? NCH / 64 : NW;   // waves that issue the HBM->LDS loads
+  static constexpr int NT = 64 * LWAVES;          // lanes that issue them
+  static constexpr int LOADS = NCH / NT;          // loads per lane, tile and tensor
   static constexpr bool SPLIT_P = (KIND == KBF16);  // bf16: P = hi + lo
   static constexpr int SMEM = 2 * NB * TILE;      // K ring, then V ring
-  static_assert(NB == 2 || NB == 3, "two or three buffers");
-  static_assert(NCH % 64 == 0 && (NCH >= NT ? NCH % NT == 0 : true), "tile must split evenly over the lanes");
+  static_assert(NB >= 2 && (NB - 2) * 2 * LOADS < 64, "ring depth: the loads in flight must fit the vmcnt field");
+  static_assert(NCH % 64 == 0 && NCH % NT == 0 && (NT & (NT - 1)) == 0, "tile must split evenly over the lanes");
   static_assert((NT / C) % 16 == 0, "swizzle period must divide the rows per load");
 
   typedef typename std::conditional<F8, i32x8, u32x4>::type qfrag_t;
@@ -289,7 +289,7 @@ struct FwdTile {
   float c;                          // softmax scale in log2 units (fp8: times dq * dk)
 
   qfrag_t qf[NDS];
-  uint32_t kaddr[NDS];              // K fragment addresses (buffer 0, key block 0)
+  uint32_t kaddr0;                  // K fragment address of k-step 0 (buffer 0)
   uint32_t vaddr[NDB][F8 ? 1 : 2];  // V transposing-read addresses (buffer 0, step 0)
   uint32_t goff_k, goff_v;          // this lane's byte offsets in a full tile (first load)
   f32x16 acc_o[NDB];
@@ -324,6 +324,7 @@ struct FwdTile {
       const int64_t jl = (qw0 + 31) / BN;
       jlast = jl < jlast ? (int)jl : jlast;
     }
+    if (qw0 >= Sq) jlast = -1;   // all rows of this wave lie past Sq
 
     // Q fragments (B operand of S^T = K Q^T), kept in registers; rows past
     // Sq read the last row (their results are never stored). Negative
@@ -347,11 +348,9 @@ struct FwdTile {
     // K (ds_read_b128): row l32 of a 32-key block. 16-bit: logical chunk
     // 2*ds + hl; fp8: chunks 4*ds + 2*hl and the next one (32 codes).
     // Chunk c of row r is stored at chunk c ^ swz_k(r).
-#pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) {
-      const int ch = F8 ? 4 * ds + 2 * hl : 2 * ds + hl;
-      kaddr[ds] = lds0 + l32 * RB + ((ch ^ swz_k<RB>(l32)) << 4);
-    }
+    // The k-step part of the chunk index (ds * KSTEP) shares no bit with the
+    // rest, so the address of k-step ds is kaddr0 ^ (ds * KSTEP * 16).
+    kaddr0 = lds0 + l32 * RB + (((F8 ? 2 * hl : hl) ^ swz_k<RB>(l32)) << 4);
     // V, 16-bit (ds_read_b64_tr_b16): within each 16-lane group, lane i
     // supplies row 16*step + 4*hl + (i/4) [+8 for the second read] and
     // head-dim columns 32*db + 16*((lane/16)&1) + 4*(i%4) .. +4; the read
@@ -380,7 +379,7 @@ struct FwdTile {
         }
       }
     }
-    // HBM->LDS (lanes 0..255 only): lane chunk i*NT + tid of a tile; one
+    // HBM->LDS (lanes 0..NT-1 only): lane chunk i*NT + tid of a tile; one
     // wave writes a contiguous KiB of LDS per instruction, so the swizzle is
     // applied to the global source offset. Load i covers rows r + i*NT/C;
     // the swizzle only depends on the row mod 16, so every load of a lane
@@ -398,7 +397,7 @@ struct FwdTile {
     l_run = 0.f;
   }
 
-  // ---- HBM -> LDS: tile j of K or V into buffer buf (lanes 0..255) ----
+  // ---- HBM -> LDS: tile j of K or V into buffer buf (lanes 0..NT-1) ----
   // Rows past Sk read the last row (only the final tile can have them).
   template <bool IS_V>
   __device__ __forceinline__ void load_one(int j, int buf) {
@@ -463,6 +462,8 @@ struct FwdTile {
   // tile instead of once per MFMA.
   typedef typename std::conditional<F8, i32x8, u32x4>::type kfrag_t;
 
+  static constexpr int KSTEP = F8 ? 4 : 2;   // chunks per k-step
+
   template <int BUF>
   __device__ __forceinline__ void read_k(kfrag_t (&kf)[NKB][NDS]) {
     constexpr uint32_t koff = BUF * TILE;
@@ -470,12 +471,13 @@ struct FwdTile {
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
       for (int ds = 0; ds < NDS; ++ds) {
+        const uint32_t ka = kaddr0 ^ (uint32_t)(ds * KSTEP * 16);
         if constexpr (F8) {
-          const u32x4 a = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
-          const u32x4 b = lds_load<u32x4>((kaddr[ds] ^ 16) + koff + kb * 32 * RB);
+          const u32x4 a = lds_load<u32x4>(ka + koff + kb * 32 * RB);
+          const u32x4 b = lds_load<u32x4>((ka ^ 16) + koff + kb * 32 * RB);
           kf[kb][ds] = (i32x8){(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
         } else {
-          kf[kb][ds] = lds_load<u32x4>(kaddr[ds] + koff + kb * 32 * RB);
+          kf[kb][ds] = lds_load<u32x4>(ka + koff + kb * 32 * RB);
         }
       }
     }
@@ -542,12 +544,13 @@ struct FwdTile {
     // Online softmax (log2 domain) with a reference maximum m_run: P =
     // exp2(S*c - m_run), O and l accumulate relative to it, and moving it
     // rescales O and l by exp2(m_old - m_new). While a row has few
-    // effective keys (l < 2^6 in units of its largest P) the reference
-    // follows the running maximum exactly, so the largest P is exactly 1 and
-    // carries no fp16 rounding error. Once l is large, a new maximum within
-    // log2(l) - 6 (at most 8) of the reference keeps the reference: that P is
-    // at most l / 64, so its rounding error weighs at most 2^-17 of O, and
-    // most tiles of long rows skip the rescale.
+    // comparable keys (this lane's part of l below 4, in units of the
+    // reference) the reference follows the running maximum exactly, so the
+    // largest P is exactly 1 and carries no fp16 rounding error: with only
+    // a few keys of similar weight, that error would not average out. After
+    // that, a new maximum less than 2 above the reference keeps it (P then
+    // stays below 4, its rounding stays relative), which skips the rescale
+    // on most tiles of long rows.
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
@@ -555,9 +558,9 @@ struct FwdTile {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = wave_max_halves(mx);
     const float m_cand = fmaxf(m_run, mx * c);
-    // slack in log2 units: clamp(log2(l) - 6, 0, 8); l of this lane's half
-    // of the keys bounds the row's l from below
-    const float slack = __builtin_amdgcn_fmed3f(__builtin_amdgcn_logf(l_run) - 6.0f, 0.0f, 8.0f);
+    // slack in log2 units; l of this lane's half of the keys bounds the
+    // row's l from below
+    const float slack = l_run >= 4.0f ? 2.0f : 0.0f;
     if (__builtin_amdgcn_ballot_w64(m_cand > m_run + slack) != 0) {
       const float m_new = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -640,20 +643,25 @@ struct FwdTile {
     tile<BUF>(j);
   }
 
+  // steps j+B .. j+NB-1 (tile j+b in buffer b); false once past the last tile
+  template <int B>
+  __device__ __forceinline__ bool steps_from(int j) {
+    if constexpr (B == NB) {
+      return true;
+    } else {
+      if (j + B >= ntiles) return false;
+      step<B>(j + B);
+      return steps_from<B + 1>(j);
+    }
+  }
+
   __device__ __forceinline__ void run() {
     // tile j lives in buffer j % NB; tiles j+1 .. j+NB-1 are in flight
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
       if (i < ntiles) load_tile(i, i);
-    for (int j = 0; j < ntiles; j += NB) {
-      step<0>(j);
-      if (j + 1 >= ntiles) break;
-      step<1>(j + 1);
-      if constexpr (NB == 3) {
-        if (j + 2 >= ntiles) break;
-        step<2>(j + 2);
-      }
-    }
+    for (int j = 0; j < ntiles; j += NB)
+      if (!steps_from<0>(j)) break;
     store();
   }
 
@@ -688,15 +696,20 @@ struct FwdTile {
 };
 
 // 32-key tiles in a ring of FA_NBUF buffers per tensor: 2 x 3 x 32 x D x 2
-// bytes (48 KiB at D = 128), so three 4-wave workgroups (three waves per
-// SIMD) fit in the 160 KiB of LDS of a CU, and the register budget is
-// capped to match.
+// bytes (48 KiB at D = 128). At least three waves per SIMD, so the register
+// budget is capped at a third of the file.
 #ifndef FA_NBUF
 #define FA_NBUF 3
 #endif
+// Waves per workgroup (32 query rows each). Four, i.e. three workgroups per
+// CU, except for causal D = 64, where 8-wave workgroups run faster (half
+// as many K/V tiles loaded per query row, and four waves per SIMD still fit
+// the register budget at that head dim).
+__host__ __device__ constexpr int waves_for(int d, bool causal) { return (causal && d == 64) ? 8 : 4; }
+
 template <int D, bool CAUSAL, int KIND, int OUT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void fa_fwd_kernel(Params p) {
-  using Blk = FwdTile<D, 32, FA_NBUF, CAUSAL, KIND, OUT>;
+__global__ __launch_bounds__(64 * waves_for(D, CAUSAL)) __attribute__((amdgpu_waves_per_eu(3))) void fa_fwd_kernel(Params p) {
+  using Blk = FwdTile<D, 32, waves_for(D, CAUSAL), FA_NBUF, CAUSAL, KIND, OUT>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
@@ -790,7 +803,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (B > lim / H || Sq > lim || Sk > lim) return FA_ERR_BAD_SHAPE;
   const int64_t BH = B * H;
   if (BH > (lim / Sq) || BH > (lim / Sk)) return FA_ERR_BAD_SHAPE;
-  const int64_t nqb = (Sq + 127) / 128;   // 128 query rows per workgroup
+  const int nw = fa::waves_for((int)D, causal != 0);
+  const int64_t nqb = (Sq + 32 * nw - 1) / (32 * nw);   // 32 * nw query rows per workgroup
   if (nqb > INT32_MAX || BH * nqb > INT32_MAX) return FA_ERR_BAD_SHAPE;
 
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return FA_ERR_MISALIGNED;
@@ -834,7 +848,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   }
   if (!fn) return FA_ERR_UNSUPPORTED_DTYPE;
 
-  hipLaunchKernelGGL(fn, dim3((unsigned)p.total), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(fn, dim3((unsigned)p.total), dim3(64 * nw), 0, stream, p);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }

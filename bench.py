@@ -4,8 +4,8 @@ MFMA peak on B4 H32 Sq=Sk=4096 D128 fp16, BNSD, non-causal, one GPU.
 One step = one fa_fwd call over the whole batch (inputs resident in HBM).
 Prints one JSON line. Options:
   --gpus N      only N=1 is supported (one process, one GPU)
-  --steps K     timed steps (default 20)
-  --warmup W    untimed steps first (default 3)
+  --steps K     timed steps (default 50)
+  --warmup W    untimed steps first (default 30: the clocks settle under load)
   --workload I  index into the workload list (default: the headline, 2)
   --no-cpu      skip the CPU-oracle baseline leg
   --cpu-seconds approximate CPU budget for the oracle leg (default 15)
@@ -94,8 +94,8 @@ def cpu_baseline(cfg, inp, budget_s: float):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -48,6 +48,11 @@ def test_scale_variants(dtype):
 
 
 def _heads_to_check(cfg, rng):
+    """Whole heads checked on every row, and heads checked on sampled rows.
+    With large logits (amp > 1) the fp16 rounding of P leaves the least
+    margin to the tolerance, so every head is checked whole."""
+    if cfg.amp != 1.0:
+        return [(b, h) for b in range(cfg.B) for h in range(cfg.H)], []
     bh = [(0, 0), (cfg.B - 1, cfg.H - 1)]
     extra = [(int(rng.integers(cfg.B)), int(rng.integers(cfg.H))) for _ in range(4)]
     return bh, extra
@@ -59,21 +64,27 @@ def test_workload_full_size(idx):
     inp = fi.make_inputs(cfg)
     rng = np.random.default_rng(idx)
     whole, sampled = _heads_to_check(cfg, rng)
-    for od in (fi.F32, cfg.o_dtype):
-        o, lse = run_gpu(cfg, inp, od)
-        # properties at every row: finite, lse >= the scaled score of key 0
-        # (key 0 is visible to every row under either mask)
-        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
-        q0 = fi.as_float64(inp.q[..., :, :], inp.descale_q)
-        k0 = fi.as_float64(inp.k[..., :1, :], inp.descale_k)
-        s0 = np.einsum("bhsd,bhd->bhs", q0, k0[:, :, 0, :]) * cfg.scale
-        assert np.all(lse >= s0 - 1e-3)
-        for (b, h) in whole:
-            rows = np.arange(cfg.Sq)
-            ro, rl = oracle_rows(cfg, inp, b, h, rows)
-            compare(cfg, od, o[b, h], lse[b, h], ro, rl, what=f"{cfg.name} {od} head {b},{h}")
-        for (b, h) in sampled:
-            rows = sample_rows(cfg.Sq, rng)
-            ro, rl = oracle_rows(cfg, inp, b, h, rows)
-            compare(cfg, od, o[b, h, rows], lse[b, h, rows], ro, rl,
-                    what=f"{cfg.name} {od} rows of {b},{h}")
+    ods = (fi.F32, cfg.o_dtype)
+    outs = {od: run_gpu(cfg, inp, od) for od in ods}
+    # properties at every row: finite, lse >= the scaled score of key 0
+    # (key 0 is visible to every row under either mask)
+    q0 = fi.as_float64(inp.q, inp.descale_q)
+    k0 = fi.as_float64(inp.k[..., :1, :], inp.descale_k)
+    s0 = np.einsum("bhsd,bhd->bhs", q0, k0[:, :, 0, :]) * cfg.scale
+    for od, (o, lse) in outs.items():
+        assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse)), od
+        assert np.all(lse >= s0 - 1e-3), od
+    worst = {od: 0.0 for od in ods}
+    for (b, h) in whole:
+        ro, rl = oracle_rows(cfg, inp, b, h, np.arange(cfg.Sq))
+        for od, (o, lse) in outs.items():
+            e, _ = compare(cfg, od, o[b, h], lse[b, h], ro, rl, what=f"{cfg.name} {od} head {b},{h}")
+            worst[od] = max(worst[od], e)
+    for (b, h) in sampled:
+        rows = sample_rows(cfg.Sq, rng)
+        ro, rl = oracle_rows(cfg, inp, b, h, rows)
+        for od, (o, lse) in outs.items():
+            e, _ = compare(cfg, od, o[b, h, rows], lse[b, h, rows], ro, rl,
+                           what=f"{cfg.name} {od} rows of {b},{h}")
+            worst[od] = max(worst[od], e)
+    print(f"{cfg.name}: max |dO| over checked rows {worst}")
