@@ -502,9 +502,7 @@ struct FwdTile {
     kfrag_t kf[NKB][NDS];
     read_k<BUF>(kf);
     mma_s(kf, s);
-#ifndef KPIPE
-#define KPIPE 4
-#endif
+    constexpr int KPIPE = 4;
     if constexpr (!F8 && NKB == 1 && NDS > KPIPE) {
       // KPIPE reads in flight ahead of the MFMA that consumes them.
       __builtin_amdgcn_sched_group_barrier(0x100, KPIPE, 0);
@@ -518,7 +516,7 @@ struct FwdTile {
   }
 
   // ---- mask, online softmax and P for tile j ----
-  __device__ __forceinline__ void softmax(int j, f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1]) {
+  __device__ __forceinline__ void mask_s(int j, f32x16 (&s)[NKB]) {
     const int64_t kt0 = (int64_t)j * BN;
     // mask: keys past Sk, keys above the diagonal. key = kt0 + kb*32 +
     // 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or > this row's query:
@@ -540,7 +538,9 @@ struct FwdTile {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kb][r] = (kb * 32 + 8 * (r >> 2) + (r & 3)) >= lim ? -INFINITY : s[kb][r];
     }
+  }
 
+  __device__ __forceinline__ void rescale_s(const f32x16 (&s)[NKB]) {
     // Online softmax (log2 domain) with a reference maximum m_run: P =
     // exp2(S*c - m_run), O and l accumulate relative to it, and moving it
     // rescales O and l by exp2(m_old - m_new). While a row has few
@@ -569,8 +569,10 @@ struct FwdTile {
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
       m_run = m_cand;
     }
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
+  }
 
+  __device__ __forceinline__ void exp_p(const f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1]) {
+    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -592,6 +594,12 @@ struct FwdTile {
         if constexpr (SPLIT_P) pl[kb * 2 + half] = g;
       }
     }
+  }
+
+  __device__ __forceinline__ void softmax(int j, f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1]) {
+    mask_s(j, s);
+    rescale_s(s);
+    exp_p(s, pf, pl);
   }
 
   // ---- O^T += V^T P^T for one tile (buffer BUF); the V fragments of step
