@@ -26,11 +26,13 @@ FA_ERR_BAD_SCALE = 7
 FA_ERR_MISALIGNED = 8
 FA_ERR_ALIASING = 9
 FA_ERR_HIP = 10
+FA_ERR_WORKSPACE = 11
 
 FA_LAYOUT_BNSD = 0
 FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
 
-EXPORTS = ("fa_fwd", "fa_status_str", "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_status_str",
+           "fa_abi_version")
 
 _lib = None
 
@@ -57,6 +59,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            ctypes.c_int, ctypes.c_int,    # in_dtype o_dtype
                            vp, vp, vp,                    # descale q k v
                            vp]                            # stream
+    lib.fa_fwd_splitkv.restype = ctypes.c_int
+    lib.fa_fwd_splitkv.argtypes = lib.fa_fwd.argtypes[:-1] + [ctypes.c_int, vp, i64, vp]
+    lib.fa_fwd_splitkv_workspace_size.restype = i64
+    lib.fa_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
     lib.fa_status_str.argtypes = [ctypes.c_int]
     lib.fa_abi_version.restype = ctypes.c_int
@@ -76,6 +82,22 @@ def fa_fwd_raw(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_pro
     return load_library().fa_fwd(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale,
                                  causal, keep_prob, in_dtype, o_dtype,
                                  descale_q, descale_k, descale_v, stream)
+
+
+def fa_fwd_splitkv_raw(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_prob,
+                       in_dtype, o_dtype, descale_q, descale_k, descale_v, num_splits,
+                       workspace, workspace_size, stream) -> int:
+    """The split-KV C entry point with integer pointers; returns the status code."""
+    return load_library().fa_fwd_splitkv(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale,
+                                         causal, keep_prob, in_dtype, o_dtype, descale_q,
+                                         descale_k, descale_v, num_splits, workspace,
+                                         workspace_size, stream)
+
+
+def splitkv_workspace_size(B, H, Sq, Sk, D, causal=False, num_splits=0) -> int:
+    """Workspace bytes fa_fwd_splitkv needs (0: a single range; -1: rejected sizes)."""
+    return load_library().fa_fwd_splitkv_workspace_size(B, H, Sq, Sk, D, 1 if causal else 0,
+                                                        num_splits)
 
 
 def _dtype_code(dt) -> int:
@@ -107,6 +129,24 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
     ``o_dtype`` (default: fp16 for fp16/fp8 inputs, bf16 for bf16 inputs),
     lse [B,H,Sq] fp32 (natural-log logsumexp of the scaled, masked scores).
     """
+    return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
+                 out, lse, stream, None, None)
+
+
+def fa_fwd_splitkv(q, k, v, *, num_splits: int = 0, scale: float | None = None,
+                   causal: bool = False, keep_prob: float = 1.0, o_dtype=None, descale_q=None,
+                   descale_k=None, descale_v=None, out=None, lse=None, workspace=None,
+                   stream=None):
+    """fa_fwd with the keys of each query block split into ``num_splits``
+    ranges (0: chosen to fill the GPU), merged by logsumexp. ``workspace``:
+    an optional uint8 GPU tensor of at least ``splitkv_workspace_size(...)``
+    bytes (allocated here when not given)."""
+    return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
+                 out, lse, stream, int(num_splits), workspace)
+
+
+def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
+          out, lse, stream, num_splits, workspace):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -136,9 +176,23 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
     dv = descale_v.data_ptr() if descale_v is not None else None
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    code = fa_fwd_raw(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                      lse.data_ptr(), B, H, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale),
-                      1 if causal else 0, float(keep_prob), in_code,
-                      _dtype_code(out.dtype), dq, dk, dv, stream)
-    _check_status(code)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, H, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale), 1 if causal else 0,
+            float(keep_prob), in_code, _dtype_code(out.dtype), dq, dk, dv)
+    if num_splits is None:
+        _check_status(fa_fwd_raw(*args, stream))
+        return out, lse
+    need = splitkv_workspace_size(B, H, Sq, Sk, D, causal, num_splits)
+    if need < 0:
+        raise ValueError("FA_ERR_BAD_SHAPE")
+    if workspace is None and need > 0:
+        # 256 extra bytes so the start can be aligned to 256
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    if workspace is not None:
+        base = workspace.data_ptr()
+        ws = (base + 255) // 256 * 256
+        ws_size = workspace.numel() - (ws - base)
+    else:
+        ws, ws_size = None, 0
+    _check_status(fa_fwd_splitkv_raw(*args, num_splits, ws, ws_size, stream))
     return out, lse

@@ -74,6 +74,10 @@ struct Params {
   int32_t total;        // B * H * nqb workgroups
   float scale_log2;     // |scale| * log2(e)
   int32_t negate;       // scale < 0: Q fragments are negated (exact)
+  // split-KV only: key-tile ranges per query block, partial results
+  int32_t nsplit;       // ranges per query block (workgroups per block)
+  float* ws_o;          // [nsplit][B*H*Sq][D] fp32, O of each range (normalised)
+  float* ws_lse;        // [nsplit][B*H*Sq] fp32, lse of each range (-inf: no key)
 };
 
 template <typename T>
@@ -251,7 +255,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // for fp16 inputs, and the V codes, read transposed from LDS with
 // ds_read_b64_tr_b8, are converted exactly to fp16 (every e4m3fn value is
 // an fp16 value); the descale of V multiplies O in the epilogue.
-template <int D, int BN_, int NW_, int NB_, bool CAUSAL, int KIND, int OUT>
+template <int D, int BN_, int NW_, int NB_, bool CAUSAL, int KIND, int OUT, bool SPLIT>
 struct FwdTile {
   static constexpr bool F8 = (KIND == KFP8);
   static constexpr int MK = F8 ? KF16 : KIND;     // type of the P.V product
@@ -282,7 +286,8 @@ struct FwdTile {
   const Params& p;
   uint32_t lds0;                    // LDS byte address of the tile buffers
   int tid, lane, wave, hl, l32;
-  int bh, ntiles, jlast;
+  int bh, jbeg, ntiles, jlast;     // tiles jbeg .. ntiles-1 of this block (split-KV: one range)
+  int split;
   int64_t Sq, Sk, q0, qw0, qrow;
   const char* khead;
   const char* vhead;
@@ -302,7 +307,12 @@ struct FwdTile {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hl = lane >> 5;
     l32 = lane & 31;
-    const int t = xcd_remap(blockIdx.x, p.total);
+    int t = xcd_remap(blockIdx.x, p.total);
+    split = 0;
+    if constexpr (SPLIT) {
+      split = t % p.nsplit;          // the ranges of a block are adjacent, on one XCD
+      t /= p.nsplit;
+    }
     bh = t / p.nqb;
     int qb = t - bh * p.nqb;
     if constexpr (CAUSAL) qb = p.nqb - 1 - qb;   // longest rows first
@@ -319,6 +329,15 @@ struct FwdTile {
     int64_t kend = Sk;
     if constexpr (CAUSAL) kend = (q0 + BM) < Sk ? (q0 + BM) : Sk;
     ntiles = (int)((kend + BN - 1) / BN);
+    jbeg = 0;
+    if constexpr (SPLIT) {
+      // range `split` of nsplit near-equal ranges of the block's tiles
+      // (empty when there are more ranges than tiles)
+      const int per = (ntiles + p.nsplit - 1) / p.nsplit;
+      jbeg = split * per;
+      ntiles = jbeg + per < ntiles ? jbeg + per : ntiles;
+      if (jbeg > ntiles) jbeg = ntiles;
+    }
     jlast = ntiles - 1;   // last tile this wave needs
     if constexpr (CAUSAL) {
       const int64_t jl = (qw0 + 31) / BN;
@@ -651,7 +670,8 @@ struct FwdTile {
     tile<BUF>(j);
   }
 
-  // steps j+B .. j+NB-1 (tile j+b in buffer b); false once past the last tile
+  // steps j+B .. j+NB-1 (tile j+b in buffer b, counting from jbeg); false
+  // once past the last tile
   template <int B>
   __device__ __forceinline__ bool steps_from(int j) {
     if constexpr (B == NB) {
@@ -664,11 +684,11 @@ struct FwdTile {
   }
 
   __device__ __forceinline__ void run() {
-    // tile j lives in buffer j % NB; tiles j+1 .. j+NB-1 are in flight
+    // tile j lives in buffer (j - jbeg) % NB; tiles j+1 .. j+NB-1 are in flight
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
-      if (i < ntiles) load_tile(i, i);
-    for (int j = 0; j < ntiles; j += NB)
+      if (jbeg + i < ntiles) load_tile(jbeg + i, i);
+    for (int j = jbeg; j < ntiles; j += NB)
       if (!steps_from<0>(j)) break;
     store();
   }
@@ -676,6 +696,10 @@ struct FwdTile {
   // ---- epilogue: O = O / l (fp8: times the V descale), lse = (m + log2 l) * ln 2 ----
   __device__ __forceinline__ void store() {
     const float l_tot = wave_sum_halves(l_run);
+    if constexpr (SPLIT) {
+      store_partial(l_tot);
+      return;
+    }
     float inv_l = 1.f / l_tot;
     if constexpr (F8) inv_l *= *p.descale_v;
     if (qrow >= Sq) return;
@@ -701,7 +725,73 @@ struct FwdTile {
       p.lse[(int64_t)bh * Sq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
     }
   }
+
+  // split-KV epilogue: this range's O (normalised by its own l; fp8: times
+  // the V descale) and lse, fp32; a row that saw no key in the range gets
+  // O = 0 and lse = -inf, which the merge weighs by exp(-inf) = 0.
+  __device__ __forceinline__ void store_partial(float l_tot) {
+    if (qrow >= Sq) return;
+    const bool any = l_tot > 0.f;
+    float inv_l = any ? 1.f / l_tot : 0.f;
+    if constexpr (F8) inv_l *= *p.descale_v;
+    const int64_t rows = (int64_t)(p.total / p.nsplit / p.nqb) * Sq;   // B*H*Sq
+    const int64_t r = (int64_t)split * rows + (int64_t)bh * Sq + qrow;
+    float* orow = p.ws_o + r * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * hl;
+        *(f32x4*)(orow + d) = (f32x4){acc_o[db][4 * g + 0] * inv_l, acc_o[db][4 * g + 1] * inv_l,
+                                      acc_o[db][4 * g + 2] * inv_l, acc_o[db][4 * g + 3] * inv_l};
+      }
+    }
+    if (hl == 0)
+      p.ws_lse[r] = any ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
+  }
 };
+
+// ---- split-KV merge: for each row, lse = ln sum_s exp(lse_s) and
+// O = sum_s exp(lse_s - lse) * O_s over the nsplit ranges (every row sees
+// key 0 in some range, so at least one lse_s is finite). One lane per four
+// head-dim entries of a row; memory-bound. ----
+struct MergeParams {
+  const float* ws_o;
+  const float* ws_lse;
+  char* o;
+  float* lse;
+  int64_t rows;         // B*H*Sq
+  int32_t nsplit;
+};
+
+template <int D, int OUT>
+__global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
+  constexpr int TPR = D / 4;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / TPR;
+  const int d = (int)(gid % TPR) * 4;
+  if (row >= p.rows) return;
+  float m = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, p.ws_lse[(int64_t)s * p.rows + row]);
+  float sum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < p.nsplit; ++s) {
+    const int64_t r = (int64_t)s * p.rows + row;
+    const float w = expf(p.ws_lse[r] - m);
+    if (w == 0.f) continue;          // range without a key (its O is 0 anyway)
+    sum += w;
+    acc += w * *(const f32x4*)(p.ws_o + r * D + d);
+  }
+  const float inv = 1.f / sum;
+  acc *= inv;
+  if constexpr (OUT == OF32) {
+    *(f32x4*)(p.o + (row * D + d) * 4) = acc;
+  } else {
+    constexpr int PK = (OUT == OBF16) ? KBF16 : KF16;
+    *(u32x2*)(p.o + (row * D + d) * 2) = (u32x2){pack2<PK>(acc[0], acc[1]), pack2<PK>(acc[2], acc[3])};
+  }
+  if (d == 0) p.lse[row] = m + logf(sum);
+}
 
 // 32-key tiles in a ring of FA_NBUF buffers per tensor: 2 x 3 x 32 x D x 2
 // bytes (48 KiB at D = 128). At least three waves per SIMD, so the register
@@ -715,9 +805,9 @@ struct FwdTile {
 // the register budget at that head dim).
 __host__ __device__ constexpr int waves_for(int d, bool causal) { return (causal && d == 64) ? 8 : 4; }
 
-template <int D, bool CAUSAL, int KIND, int OUT>
+template <int D, bool CAUSAL, int KIND, int OUT, bool SPLIT>
 __global__ __launch_bounds__(64 * waves_for(D, CAUSAL)) __attribute__((amdgpu_waves_per_eu(3))) void fa_fwd_kernel(Params p) {
-  using Blk = FwdTile<D, 32, waves_for(D, CAUSAL), FA_NBUF, CAUSAL, KIND, OUT>;
+  using Blk = FwdTile<D, 32, waves_for(D, CAUSAL), FA_NBUF, CAUSAL, KIND, OUT, SPLIT>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
@@ -731,20 +821,21 @@ namespace {
 
 using fa::Params;
 typedef void (*KernelFn)(Params);
+typedef void (*MergeFn)(fa::MergeParams);
 
-template <int D, bool CAUSAL, int KIND, int OUT>
+template <int D, bool CAUSAL, int KIND, int OUT, bool SPLIT>
 KernelFn pick() {
-  return fa::fa_fwd_kernel<D, CAUSAL, KIND, OUT>;
+  return fa::fa_fwd_kernel<D, CAUSAL, KIND, OUT, SPLIT>;
 }
 
-template <int D, int KIND, int OUT>
+template <int D, int KIND, int OUT, bool SPLIT>
 KernelFn pick_c(bool causal) {
-  return causal ? pick<D, true, KIND, OUT>() : pick<D, false, KIND, OUT>();
+  return causal ? pick<D, true, KIND, OUT, SPLIT>() : pick<D, false, KIND, OUT, SPLIT>();
 }
 
-template <int KIND, int OUT>
+template <int KIND, int OUT, bool SPLIT>
 KernelFn pick_d(int64_t D, bool causal) {
-  return D == 64 ? pick_c<64, KIND, OUT>(causal) : pick_c<128, KIND, OUT>(causal);
+  return D == 64 ? pick_c<64, KIND, OUT, SPLIT>(causal) : pick_c<128, KIND, OUT, SPLIT>(causal);
 }
 
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -761,35 +852,23 @@ int64_t dtype_size(fa_dtype_t t) {
   return 0;
 }
 
-}  // namespace
+// Everything fa_fwd and fa_fwd_splitkv check before any HIP call, and the
+// launch parameters that follow from the arguments.
+struct Call {
+  Params p;
+  int nw;               // waves per workgroup
+  int64_t BH, nqb, D;
+  bool causal;
+  fa_dtype_t in_dtype, o_dtype;
+  int64_t nq, nk, no, nl;   // byte sizes of q, k (and v), o, lse
+};
 
-extern "C" {
-
-int fa_abi_version(void) { return FA_ABI_VERSION; }
-
-const char* fa_status_str(fa_status_t s) {
-  switch (s) {
-    case FA_OK: return "FA_OK";
-    case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER";
-    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE";
-    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM";
-    case FA_ERR_UNSUPPORTED_DTYPE: return "FA_ERR_UNSUPPORTED_DTYPE";
-    case FA_ERR_UNSUPPORTED_LAYOUT: return "FA_ERR_UNSUPPORTED_LAYOUT";
-    case FA_ERR_UNSUPPORTED_DROPOUT: return "FA_ERR_UNSUPPORTED_DROPOUT";
-    case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE";
-    case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED";
-    case FA_ERR_ALIASING: return "FA_ERR_ALIASING";
-    case FA_ERR_HIP: return "FA_ERR_HIP";
-  }
-  return "FA_ERR_UNKNOWN";
-}
-
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                   fa_layout_t layout, float scale, int causal, float keep_prob,
-                   fa_dtype_t in_dtype, fa_dtype_t o_dtype,
-                   const float* descale_q, const float* descale_k, const float* descale_v,
-                   hipStream_t stream) {
+fa_status_t check_call(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                       fa_layout_t layout, float scale, int causal, float keep_prob,
+                       fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                       const float* descale_q, const float* descale_k, const float* descale_v,
+                       Call& c) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_BAD_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
@@ -819,14 +898,16 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if ((uintptr_t)lse & 3) return FA_ERR_MISALIGNED;
 
   const int64_t ie = dtype_size(in_dtype), oe = dtype_size(o_dtype);
-  const int64_t nq = BH * Sq * D * ie, nk = BH * Sk * D * ie;
-  const int64_t no = BH * Sq * D * oe, nl = BH * Sq * 4;
-  if (overlaps(o, no, q, nq) || overlaps(o, no, k, nk) || overlaps(o, no, v, nk) ||
-      overlaps(lse, nl, q, nq) || overlaps(lse, nl, k, nk) || overlaps(lse, nl, v, nk) ||
-      overlaps(o, no, lse, nl))
+  c.nq = BH * Sq * D * ie;
+  c.nk = BH * Sk * D * ie;
+  c.no = BH * Sq * D * oe;
+  c.nl = BH * Sq * 4;
+  if (overlaps(o, c.no, q, c.nq) || overlaps(o, c.no, k, c.nk) || overlaps(o, c.no, v, c.nk) ||
+      overlaps(lse, c.nl, q, c.nq) || overlaps(lse, c.nl, k, c.nk) || overlaps(lse, c.nl, v, c.nk) ||
+      overlaps(o, c.no, lse, c.nl))
     return FA_ERR_ALIASING;
 
-  Params p;
+  Params& p = c.p;
   p.q = (const char*)q;
   p.k = (const char*)k;
   p.v = (const char*)v;
@@ -844,19 +925,158 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   // to exp2(0) = 1) and keeps -inf masks intact.
   p.scale_log2 = fmaxf(fabsf(scale) * 1.4426950408889634f, FLT_MIN);
   p.negate = scale < 0.f;
+  p.nsplit = 1;
+  p.ws_o = nullptr;
+  p.ws_lse = nullptr;
+  c.nw = nw;
+  c.BH = BH;
+  c.nqb = nqb;
+  c.D = D;
+  c.causal = causal != 0;
+  c.in_dtype = in_dtype;
+  c.o_dtype = o_dtype;
+  return FA_OK;
+}
 
-  const bool cz = causal != 0;
-  KernelFn fn = nullptr;
-  if (in_dtype == FA_F16) {
-    fn = (o_dtype == FA_F32) ? pick_d<fa::KF16, fa::OF32>(D, cz) : pick_d<fa::KF16, fa::OF16>(D, cz);
-  } else if (in_dtype == FA_BF16) {
-    fn = (o_dtype == FA_F32) ? pick_d<fa::KBF16, fa::OF32>(D, cz) : pick_d<fa::KBF16, fa::OBF16>(D, cz);
-  } else if (in_dtype == FA_FP8_E4M3) {
-    fn = (o_dtype == FA_F32) ? pick_d<fa::KFP8, fa::OF32>(D, cz) : pick_d<fa::KFP8, fa::OF16>(D, cz);
+template <bool SPLIT>
+KernelFn pick_kernel(const Call& c) {
+  if (SPLIT) {   // partial results are fp32 whatever the output type
+    if (c.in_dtype == FA_F16) return pick_d<fa::KF16, fa::OF32, SPLIT>(c.D, c.causal);
+    if (c.in_dtype == FA_BF16) return pick_d<fa::KBF16, fa::OF32, SPLIT>(c.D, c.causal);
+    return pick_d<fa::KFP8, fa::OF32, SPLIT>(c.D, c.causal);
   }
-  if (!fn) return FA_ERR_UNSUPPORTED_DTYPE;
+  if (c.in_dtype == FA_F16)
+    return (c.o_dtype == FA_F32) ? pick_d<fa::KF16, fa::OF32, false>(c.D, c.causal) : pick_d<fa::KF16, fa::OF16, false>(c.D, c.causal);
+  if (c.in_dtype == FA_BF16)
+    return (c.o_dtype == FA_F32) ? pick_d<fa::KBF16, fa::OF32, false>(c.D, c.causal) : pick_d<fa::KBF16, fa::OBF16, false>(c.D, c.causal);
+  return (c.o_dtype == FA_F32) ? pick_d<fa::KFP8, fa::OF32, false>(c.D, c.causal) : pick_d<fa::KFP8, fa::OF16, false>(c.D, c.causal);
+}
 
-  hipLaunchKernelGGL(fn, dim3((unsigned)p.total), dim3(64 * nw), 0, stream, p);
+MergeFn pick_merge(const Call& c) {
+  if (c.o_dtype == FA_F32) return c.D == 64 ? fa::fa_merge_kernel<64, fa::OF32> : fa::fa_merge_kernel<128, fa::OF32>;
+  if (c.o_dtype == FA_BF16) return c.D == 64 ? fa::fa_merge_kernel<64, fa::OBF16> : fa::fa_merge_kernel<128, fa::OBF16>;
+  return c.D == 64 ? fa::fa_merge_kernel<64, fa::OF16> : fa::fa_merge_kernel<128, fa::OF16>;
+}
+
+constexpr int kMaxSplits = 256;
+
+// Key ranges per query block when the caller passes num_splits = 0: enough
+// workgroups for about two rounds of the 256 CUs (three 4-wave workgroups,
+// or one 8-wave workgroup, resident per CU), each range at least four
+// 32-key tiles long.
+int auto_splits(int64_t BH, int64_t nqb, int64_t Sk, int nw) {
+  const int64_t resident = 256 * (nw == 4 ? 3 : 1);
+  const int64_t base = BH * nqb;
+  if (base >= 2 * resident) return 1;
+  int64_t s = (2 * resident + base - 1) / base;
+  const int64_t by_tiles = ((Sk + 31) / 32) / 4;
+  if (s > by_tiles) s = by_tiles;
+  if (s > 64) s = 64;
+  return s < 1 ? 1 : (int)s;
+}
+
+int64_t workspace_bytes(int64_t BH, int64_t Sq, int64_t D, int nsplit) {
+  if (nsplit <= 1) return 0;
+  const int64_t o_bytes = (int64_t)nsplit * BH * Sq * D * 4;
+  return ((o_bytes + 255) / 256) * 256 + (int64_t)nsplit * BH * Sq * 4;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return FA_ABI_VERSION; }
+
+const char* fa_status_str(fa_status_t s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE";
+    case FA_ERR_UNSUPPORTED_HEAD_DIM: return "FA_ERR_UNSUPPORTED_HEAD_DIM";
+    case FA_ERR_UNSUPPORTED_DTYPE: return "FA_ERR_UNSUPPORTED_DTYPE";
+    case FA_ERR_UNSUPPORTED_LAYOUT: return "FA_ERR_UNSUPPORTED_LAYOUT";
+    case FA_ERR_UNSUPPORTED_DROPOUT: return "FA_ERR_UNSUPPORTED_DROPOUT";
+    case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE";
+    case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED";
+    case FA_ERR_ALIASING: return "FA_ERR_ALIASING";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                   fa_layout_t layout, float scale, int causal, float keep_prob,
+                   fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                   const float* descale_q, const float* descale_k, const float* descale_v,
+                   hipStream_t stream) {
+  Call c;
+  const fa_status_t st = check_call(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_prob,
+                                    in_dtype, o_dtype, descale_q, descale_k, descale_v, c);
+  if (st != FA_OK) return st;
+  hipLaunchKernelGGL(pick_kernel<false>(c), dim3((unsigned)c.p.total), dim3(64 * c.nw), 0, stream, c.p);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  return FA_OK;
+}
+
+int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                      int causal, int num_splits) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || (D != 64 && D != 128)) return -1;
+  if (num_splits < 0 || num_splits > kMaxSplits) return -1;
+  const int64_t lim = (int64_t)1 << 40;
+  if (B > lim / H || Sq > lim || Sk > lim || B * H > lim / Sq || B * H > lim / Sk) return -1;
+  const int nw = fa::waves_for((int)D, causal != 0);
+  const int64_t nqb = (Sq + 32 * nw - 1) / (32 * nw);
+  const int ns = num_splits ? num_splits : auto_splits(B * H, nqb, Sk, nw);
+  return workspace_bytes(B * H, Sq, D, ns);
+}
+
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                           fa_layout_t layout, float scale, int causal, float keep_prob,
+                           fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                           const float* descale_q, const float* descale_k, const float* descale_v,
+                           int num_splits, void* workspace, int64_t workspace_size,
+                           hipStream_t stream) {
+  Call c;
+  const fa_status_t st = check_call(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_prob,
+                                    in_dtype, o_dtype, descale_q, descale_k, descale_v, c);
+  if (st != FA_OK) return st;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_BAD_SHAPE;
+  const int ns = num_splits ? num_splits : auto_splits(c.BH, c.nqb, Sk, c.nw);
+  if (c.BH * c.nqb * ns > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  if ((c.BH * Sq * (D / 4) + 255) / 256 > INT32_MAX) return FA_ERR_BAD_SHAPE;   // merge grid
+  const int64_t need = workspace_bytes(c.BH, Sq, D, ns);
+  if (need > 0) {
+    if (!workspace || workspace_size < need) return FA_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 255) return FA_ERR_MISALIGNED;
+    if (overlaps(workspace, need, q, c.nq) || overlaps(workspace, need, k, c.nk) ||
+        overlaps(workspace, need, v, c.nk) || overlaps(workspace, need, o, c.no) ||
+        overlaps(workspace, need, lse, c.nl))
+      return FA_ERR_ALIASING;
+  }
+  if (ns == 1) {   // one range: the plain kernel writes O and lse directly
+    hipLaunchKernelGGL(pick_kernel<false>(c), dim3((unsigned)c.p.total), dim3(64 * c.nw), 0, stream, c.p);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  Params p = c.p;
+  p.nsplit = ns;
+  p.total = (int32_t)(c.BH * c.nqb * ns);
+  p.ws_o = (float*)workspace;
+  const int64_t o_bytes = (int64_t)ns * c.BH * Sq * D * 4;
+  p.ws_lse = (float*)((char*)workspace + ((o_bytes + 255) / 256) * 256);
+  hipLaunchKernelGGL(pick_kernel<true>(c), dim3((unsigned)p.total), dim3(64 * c.nw), 0, stream, p);
+  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  fa::MergeParams m;
+  m.ws_o = p.ws_o;
+  m.ws_lse = p.ws_lse;
+  m.o = (char*)o;
+  m.lse = lse;
+  m.rows = c.BH * Sq;
+  m.nsplit = ns;
+  const int64_t lanes = m.rows * (D / 4);
+  hipLaunchKernelGGL(pick_merge(c), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, m);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
 }

@@ -35,12 +35,13 @@
  * review", chatdocs.ruinique.com/hygon/flash-attention-fixed-bugs, item 17).
  *
  * Ownership: the caller owns every buffer. The library allocates and frees
- * no device memory, never synchronises, and enqueues one kernel on `stream`
+ * no device memory, never synchronises, and enqueues its kernels on `stream`
  * before returning. q, k, v and the descales are read only; o and lse are
  * written only in their valid region [B,H,Sq,D] and [B,H,Sq].
  *
- * Errors: fa_fwd returns a status code and never throws. On any error other
- * than FA_ERR_HIP nothing is launched and the outputs are untouched.
+ * Errors: the entry points return a status code and never throw. On any
+ * error other than FA_ERR_HIP nothing is launched and the outputs are
+ * untouched.
  *
  * Thread safety: fa_fwd keeps no mutable state and may be called from
  * several threads on different streams.
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 1
+#define FA_ABI_VERSION 2
 
 typedef enum {
   FA_OK = 0,
@@ -68,7 +69,8 @@ typedef enum {
   FA_ERR_BAD_SCALE = 7,            /* scale is NaN or infinite */
   FA_ERR_MISALIGNED = 8,           /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   FA_ERR_ALIASING = 9,             /* o or lse overlaps q, k, v, or each other */
-  FA_ERR_HIP = 10                  /* the kernel launch failed */
+  FA_ERR_HIP = 10,                 /* a kernel launch failed */
+  FA_ERR_WORKSPACE = 11            /* fa_fwd_splitkv: workspace NULL or smaller than needed */
 } fa_status_t;
 
 typedef enum { FA_LAYOUT_BNSD = 0 } fa_layout_t;
@@ -94,6 +96,48 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    fa_dtype_t in_dtype, fa_dtype_t o_dtype,
                    const float* descale_q, const float* descale_k, const float* descale_v,
                    hipStream_t stream);
+
+/*
+ * fa_fwd_splitkv — the same computation as fa_fwd, with the keys of every
+ * block of query rows split into num_splits ranges that run as separate
+ * workgroups, for shapes whose blocks alone would leave most of the GPU
+ * idle (few heads, short or causal sequences). Each range writes its own
+ * normalised output O_s and logsumexp lse_s (fp32, in the workspace); a
+ * second kernel merges them: lse = ln sum_s exp(lse_s), O = sum_s
+ * exp(lse_s - lse) * O_s. This is the softmax identity for a split key set,
+ * the merge that the per-row logsumexp output exists for; the partition
+ * reduce of "Hygon FlashAttention: fixed-defect review" (item 7) combines
+ * split partitions the same way. Results equal fa_fwd's up to rounding.
+ *
+ * Arguments as fa_fwd, plus:
+ * num_splits: ranges per block of query rows, 0..256; 0 chooses a count
+ *   that fills the GPU (1 when the plain grid already does). Ranges past the
+ *   last key are empty and cost one workgroup each.
+ * workspace, workspace_size: device memory of at least
+ *   fa_fwd_splitkv_workspace_size(...) bytes, 256-byte aligned, owned by the
+ *   caller, not overlapping any other argument; its contents on entry do not
+ *   matter and on return are unspecified. May be NULL when that size is 0
+ *   (a single range: one kernel, as fa_fwd).
+ * Enqueues two kernels on `stream` (one when a single range is used).
+ * Errors as fa_fwd, plus FA_ERR_BAD_SHAPE for num_splits out of range,
+ * FA_ERR_WORKSPACE for a missing or short workspace, FA_ERR_MISALIGNED and
+ * FA_ERR_ALIASING for the workspace; nothing is launched on error.
+ */
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                           fa_layout_t layout, float scale, int causal, float keep_prob,
+                           fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                           const float* descale_q, const float* descale_k, const float* descale_v,
+                           int num_splits, void* workspace, int64_t workspace_size,
+                           hipStream_t stream);
+
+/*
+ * Bytes of workspace fa_fwd_splitkv needs for these sizes and num_splits
+ * (0: the automatic count); 0 when a single range is used; -1 for sizes or
+ * num_splits that fa_fwd_splitkv would reject. Host only; no HIP call.
+ */
+int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                      int causal, int num_splits);
 
 /* Human-readable name of a status code ("FA_OK", ...); never NULL. */
 const char* fa_status_str(fa_status_t s);

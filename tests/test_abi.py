@@ -41,10 +41,10 @@ def test_library_holds_gfx950_code():
 
 def test_abi_version_and_status_strings():
     lib = fa.load_library()
-    assert lib.fa_abi_version() == 1
-    names = [fa.status_str(c) for c in range(11)]
-    assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP"
-    assert len(set(names)) == 11
+    assert lib.fa_abi_version() == 2
+    names = [fa.status_str(c) for c in range(12)]
+    assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP" and names[11] == "FA_ERR_WORKSPACE"
+    assert len(set(names)) == 12
     assert fa.status_str(99) == "FA_ERR_UNKNOWN"
 
 
@@ -104,3 +104,47 @@ def test_python_wrapper_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.fa_fwd(x, x, x)
+
+
+# ---- split-KV entry points ----
+W = 0x70000000   # fake, 256-byte aligned workspace address
+
+
+def call_split(**over):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=64, Sk=1024, D=128,
+             layout=fa.FA_LAYOUT_BNSD, scale=0.125, causal=0, keep_prob=1.0,
+             in_dtype=fa.FA_F16, o_dtype=fa.FA_F16, descale_q=None, descale_k=None,
+             descale_v=None, num_splits=4, workspace=W, workspace_size=1 << 24, stream=None)
+    a.update(over)
+    return fa.fa_fwd_splitkv_raw(**a)
+
+
+def test_splitkv_workspace_size():
+    # 4 ranges of B*H*Sq rows: O (D fp32) padded to 256 bytes, then lse (fp32)
+    rows = 1 * 2 * 64
+    o_bytes = 4 * rows * 128 * 4
+    assert fa.splitkv_workspace_size(1, 2, 64, 1024, 128, False, 4) == o_bytes + 4 * rows * 4
+    assert fa.splitkv_workspace_size(1, 2, 64, 1024, 128, False, 1) == 0
+    # automatic count: a shape that fills the GPU needs no workspace
+    assert fa.splitkv_workspace_size(4, 32, 4096, 4096, 128, False, 0) == 0
+    assert fa.splitkv_workspace_size(1, 8, 512, 512, 64, False, 0) > 0
+    for bad in (dict(D=96), dict(num_splits=-1), dict(num_splits=257), dict(B=0)):
+        a = dict(B=1, H=2, Sq=64, Sk=1024, D=128, causal=False, num_splits=4)
+        a.update(bad)
+        assert fa.splitkv_workspace_size(**a) == -1
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(num_splits=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(num_splits=257), fa.FA_ERR_BAD_SHAPE),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_size=1024), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=W + 16), fa.FA_ERR_MISALIGNED),
+    (dict(workspace=Q), fa.FA_ERR_ALIASING),
+    (dict(workspace=O - 256), fa.FA_ERR_ALIASING),
+    (dict(keep_prob=0.5), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+])
+def test_splitkv_rejects_before_launch(over, code):
+    assert call_split(**over) == code

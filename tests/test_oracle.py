@@ -272,3 +272,23 @@ def test_pins_accept_correct_copy():
     fn = _mutant("none")
     for pin in PINS:
         pin(fn)
+
+
+def test_lse_merge_of_key_subsets():
+    """Attention over a key set equals the logsumexp-weighted merge of
+    attention over a partition of it: lse = ln sum_r exp(lse_r), O = sum_r
+    exp(lse_r - lse) O_r. This is the softmax identity the split-KV path
+    relies on; both sides here come from the oracle on different key sets
+    (no merge code is shared with the GPU path)."""
+    rng = np.random.default_rng(7)
+    q = rng.standard_normal((1, 2, 5, 8))
+    k = rng.standard_normal((1, 2, 11, 8))
+    v = rng.standard_normal((1, 2, 11, 8))
+    o_full, l_full = attention_fp64(q, k, v, 0.4, False)
+    cuts = [0, 3, 4, 11]
+    parts = [attention_fp64(q, k[:, :, a:b], v[:, :, a:b], 0.4, False)
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    lse = np.log(sum(np.exp(l) for _, l in parts))
+    o = sum(np.exp(l - lse)[..., None] * o_r for o_r, l in parts)
+    assert np.max(np.abs(lse - l_full)) < 1e-12
+    assert np.max(np.abs(o - o_full)) < 1e-12
