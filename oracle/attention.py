@@ -13,7 +13,14 @@ that FlashAttention reaches exactly, up to rounding order:
     head_dim ** -0.5 and it is applied before the mask);
   * causal mask: scores strictly above the diagonal (key j > query i,
     top-left aligned) are set to -inf (same section: the upper triangle with
-    diagonal offset 1 is filled with -inf);
+    diagonal offset 1 is filled with -inf). The variant with the diagonal
+    moved by ``offset`` (key j visible iff j <= i + offset; offset = Sk - Sq
+    aligns it to the bottom-right corner) follows the same rule; a row with
+    no visible key (only possible with a negative offset) is defined to give
+    O = 0 and lse = -inf, since the softmax of an empty set is undefined;
+  * grouped key/value heads: k and v may have H_kv heads with H_kv dividing
+    the query head count H; query head h then attends to key/value head
+    h // (H / H_kv) (H_kv = 1 shares one key/value head among all);
   * P = softmax(S) along the key axis, computed the safe way: subtract the
     row maximum before exponentiating (same page, section 6.2, the
     numerically stable softmax and its second, normalising pass);
@@ -36,21 +43,27 @@ import math
 import numpy as np
 
 
-def _check(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> None:
+def _check(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> int:
+    """Validates BNSD shapes; returns the query heads per key/value head."""
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be [B, H, S, D]")
-    if k.shape != v.shape or q.shape[:2] != k.shape[:2] or q.shape[3] != k.shape[3]:
+    if k.shape != v.shape or q.shape[0] != k.shape[0] or q.shape[3] != k.shape[3]:
         raise ValueError("shape mismatch between q, k, v")
+    if k.shape[1] < 1 or q.shape[1] % k.shape[1] != 0:
+        raise ValueError("the key/value head count must divide the query head count")
+    return q.shape[1] // k.shape[1]
 
 
 def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
                  causal: bool, rows: np.ndarray | None = None,
-                 return_p: bool = False):
+                 return_p: bool = False, offset: int = 0):
     """One (batch, head): q [Sq, D], k/v [Sk, D] float64.
 
     ``rows`` restricts the computation to those query indices (their causal
-    mask still uses the true row index). Returns (O [R, D], lse [R]) and, if
-    asked, the probability matrix P [R, Sk].
+    mask still uses the true row index). With ``causal``, key j is visible to
+    query i iff j <= i + offset. Returns (O [R, D], lse [R]) and, if asked,
+    the probability matrix P [R, Sk]; a row without a visible key gives
+    O = 0, lse = -inf and P = 0.
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -59,63 +72,76 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     s = (q[idx] @ k.T) * np.float64(scale)                       # S = scale*QK^T
     if causal:
         key = np.arange(k.shape[0])
-        s = np.where(key[None, :] > idx[:, None], -np.inf, s)      # j > i -> -inf
+        s = np.where(key[None, :] > idx[:, None] + offset, -np.inf, s)   # j > i + offset -> -inf
+    empty = np.all(np.isneginf(s), axis=1)                         # rows without a visible key
+    s = np.where(empty[:, None], 0.0, s)                           # (their result is set below)
     m = np.max(s, axis=1, keepdims=True)                           # row max
     p = np.exp(s - m)                                              # safe exp
     l = np.sum(p, axis=1, keepdims=True)                           # row sum
     p = p / l                                                      # softmax
+    p[empty] = 0.0
     o = p @ v                                                      # O = P V
     lse = m[:, 0] + np.log(l[:, 0])                                # logsumexp
+    lse[empty] = -np.inf
     if return_p:
         return o, lse, p
     return o, lse
 
 
 def attention_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                   causal: bool):
-    """Full forward over BNSD tensors: returns O [B,H,Sq,D], lse [B,H,Sq]."""
-    _check(q, k, v)
+                   causal: bool, offset: int = 0):
+    """Full forward over BNSD tensors: returns O [B,H,Sq,D], lse [B,H,Sq].
+    k and v may have fewer heads than q (grouped heads, see above)."""
+    group = _check(q, k, v)
     B, H, Sq, D = q.shape
     o = np.empty((B, H, Sq, D), np.float64)
     lse = np.empty((B, H, Sq), np.float64)
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h], v[b, h], scale, causal)
+            kv = h // group
+            o[b, h], lse[b, h] = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal,
+                                              offset=offset)
     return o, lse
 
 
 def attention_rows_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
-                        causal: bool, b: int, h: int, rows):
+                        causal: bool, b: int, h: int, rows, offset: int = 0):
     """Selected query rows of one (b, h) of a BNSD problem."""
-    _check(q, k, v)
-    return head_forward(q[b, h], k[b, h], v[b, h], scale, causal, rows=rows)
+    group = _check(q, k, v)
+    return head_forward(q[b, h], k[b, h // group], v[b, h // group], scale, causal, rows=rows,
+                        offset=offset)
 
 
-def attention_bruteforce(q, k, v, scale: float, causal: bool):
+def attention_bruteforce(q, k, v, scale: float, causal: bool, offset: int = 0):
     """Pure-Python loops, for tiny shapes only: same definition, no numpy math.
 
     Uses math.exp / math.fsum element by element.
     """
     B, H, Sq, D = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
     Sk = len(k[0][0])
+    Hkv = len(k[0])
     o = [[[[0.0] * D for _ in range(Sq)] for _ in range(H)] for _ in range(B)]
     lse = [[[0.0] * Sq for _ in range(H)] for _ in range(B)]
     for b in range(B):
         for h in range(H):
+            g = h * Hkv // H            # key/value head of query head h
             for i in range(Sq):
                 scores = []
                 for j in range(Sk):
-                    if causal and j > i:
+                    if causal and j - i > offset:
                         scores.append(-math.inf)
                     else:
-                        dot = math.fsum(float(q[b][h][i][d]) * float(k[b][h][j][d])
+                        dot = math.fsum(float(q[b][h][i][d]) * float(k[b][g][j][d])
                                         for d in range(D))
                         scores.append(scale * dot)
+                if all(s == -math.inf for s in scores):
+                    lse[b][h][i] = -math.inf            # no visible key: O stays 0
+                    continue
                 mx = max(scores)
                 e = [math.exp(s - mx) if s != -math.inf else 0.0 for s in scores]
                 tot = math.fsum(e)
                 for d in range(D):
-                    o[b][h][i][d] = math.fsum(e[j] / tot * float(v[b][h][j][d])
+                    o[b][h][i][d] = math.fsum(e[j] / tot * float(v[b][g][j][d])
                                               for j in range(Sk))
                 lse[b][h][i] = mx + math.log(tot)
     return np.array(o, np.float64), np.array(lse, np.float64)

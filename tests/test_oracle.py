@@ -292,3 +292,153 @@ def test_lse_merge_of_key_subsets():
     o = sum(np.exp(l - lse)[..., None] * o_r for o_r, l in parts)
     assert np.max(np.abs(lse - l_full)) < 1e-12
     assert np.max(np.abs(o - o_full)) < 1e-12
+
+
+# ------------- grouped key/value heads and a shifted causal diagonal -----
+# fn(q, k, v, scale, causal, offset): k and v may have fewer heads than q
+# (query head h uses key/value head h // (H / H_kv)); with causal, key j is
+# visible to query i iff j <= i + offset; a row with no visible key gives
+# O = 0 and lse = -inf.
+
+def xpin_bruteforce(fn):
+    """Tiny shapes with grouped heads and shifted diagonals against the
+    pure-Python loops."""
+    for (B, H, Hkv, Sq, Sk, D, causal, off, seed) in [
+        (1, 4, 2, 3, 5, 2, True, 2, 1), (2, 4, 1, 5, 3, 3, True, -2, 2),
+        (1, 6, 3, 4, 4, 2, False, 0, 3), (1, 2, 2, 6, 2, 2, True, -4, 4),
+        (1, 3, 1, 2, 6, 3, True, 4, 5),
+    ]:
+        q = rand((B, H, Sq, D), seed)
+        k = rand((B, Hkv, Sk, D), seed + 100)
+        v = rand((B, Hkv, Sk, D), seed + 200)
+        o, lse = fn(q, k, v, 0.6, causal, off)
+        ob, lb = attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), 0.6, causal, off)
+        assert np.max(np.abs(o - ob)) <= 1e-12
+        fin = np.isfinite(lb)
+        assert np.array_equal(np.isfinite(lse), fin)
+        assert np.max(np.abs(lse[fin] - lb[fin])) <= 1e-12 and np.all(lse[~fin] == -np.inf)
+
+
+def xpin_zero_q_bottom_right(fn):
+    """Q = 0, bottom-right diagonal (offset = Sk - Sq): row i averages keys
+    0 .. i + Sk - Sq, lse = ln(i + Sk - Sq + 1)."""
+    Sq, Sk, D = 4, 7, 3
+    q = np.zeros((1, 1, Sq, D))
+    k = rand((1, 1, Sk, D), 121)
+    v = rand((1, 1, Sk, D), 122)
+    o, lse = fn(q, k, v, 0.9, True, Sk - Sq)
+    for i in range(Sq):
+        n = i + Sk - Sq + 1
+        assert np.max(np.abs(o[0, 0, i] - v[0, 0, :n].mean(axis=0))) <= 1e-14
+        assert abs(lse[0, 0, i] - math.log(n)) <= 1e-14
+
+
+def xpin_rows_without_keys(fn):
+    """Bottom-right with Sq > Sk: the first Sq - Sk rows see no key (O = 0,
+    lse = -inf); row Sq - Sk sees key 0 only."""
+    Sq, Sk, D = 6, 3, 4
+    q = rand((1, 1, Sq, D), 131)
+    k = rand((1, 1, Sk, D), 132)
+    v = rand((1, 1, Sk, D), 133)
+    o, lse = fn(q, k, v, 0.7, True, Sk - Sq)
+    assert np.all(o[0, 0, : Sq - Sk] == 0.0) and np.all(lse[0, 0, : Sq - Sk] == -np.inf)
+    r = Sq - Sk
+    assert np.max(np.abs(o[0, 0, r] - v[0, 0, 0])) <= 1e-14
+    dot = math.fsum(q[0, 0, r, d] * k[0, 0, 0, d] for d in range(D))
+    assert abs(lse[0, 0, r] - 0.7 * dot) <= 1e-13
+
+
+def xpin_grouped_equals_repeated(fn):
+    """Grouped heads equal the same heads with each key/value head repeated
+    for its query heads."""
+    q = rand((2, 6, 5, 4), 141)
+    k = rand((2, 2, 7, 4), 142)
+    v = rand((2, 2, 7, 4), 143)
+    for causal, off in ((False, 0), (True, 0), (True, 2)):
+        a, la = fn(q, k, v, 0.5, causal, off)
+        b, lb = fn(q, np.repeat(k, 3, axis=1), np.repeat(v, 3, axis=1), 0.5, causal, off)
+        assert np.max(np.abs(a - b)) <= 1e-14 and np.max(np.abs(la - lb)) <= 1e-14
+
+
+def xpin_library_sdpa(fn):
+    """torch's scaled_dot_product_attention (fp64, CPU) with an explicit
+    boolean mask for the shifted diagonal and grouped heads; rows without a
+    visible key are left out (the library returns NaN there)."""
+    for (H, Hkv, Sq, Sk, off, seed) in [(4, 2, 9, 13, 4, 151), (4, 1, 13, 9, -4, 152),
+                                        (3, 3, 10, 10, 0, 153)]:
+        q = rand((1, H, Sq, 8), seed)
+        k = rand((1, Hkv, Sk, 8), seed + 1)
+        v = rand((1, Hkv, Sk, 8), seed + 2)
+        o, lse = fn(q, k, v, 0.3, True, off)
+        keep = torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + off
+        tq = torch.from_numpy(q)
+        tk = torch.from_numpy(np.repeat(k, H // Hkv, axis=1))
+        tv = torch.from_numpy(np.repeat(v, H // Hkv, axis=1))
+        ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=keep,
+                                                               scale=0.3).numpy()
+        rows = keep.any(dim=1).numpy()
+        assert np.max(np.abs(o[:, :, rows] - ref[:, :, rows])) <= 1e-10
+
+
+XPINS = [xpin_bruteforce, xpin_zero_q_bottom_right, xpin_rows_without_keys,
+         xpin_grouped_equals_repeated, xpin_library_sdpa]
+
+
+def _oracle_x(q, k, v, scale, causal, offset):
+    return attention_fp64(q, k, v, scale, causal, offset)
+
+
+@pytest.mark.parametrize("pin", XPINS, ids=lambda p: p.__name__)
+def test_oracle_grouped_shifted_pin(pin):
+    pin(_oracle_x)
+
+
+def _xmutant(kind):
+    """Independent scaffold for the grouped/shifted pins, with one planted
+    mistake per kind ("none": correct)."""
+    def fn(q, k, v, scale, causal, offset):
+        B, H, Sq, D = q.shape
+        Hkv, Sk = k.shape[1], k.shape[2]
+        o = np.zeros((B, H, Sq, D))
+        lse = np.full((B, H, Sq), -np.inf)
+        for b in range(B):
+            for h in range(H):
+                g = h % Hkv if kind == "kv_head_mod" else h // (H // Hkv)
+                s = q[b, h] @ k[b, g].T * scale
+                if causal:
+                    i = np.arange(Sq)[:, None]
+                    j = np.arange(Sk)[None, :]
+                    shift = {"offset_flip": -offset, "offset_ignored": 0}.get(kind, offset)
+                    s = np.where(j > i + shift, -np.inf, s)
+                for r in range(Sq):
+                    if np.all(np.isneginf(s[r])) and kind != "empty_rows_nan":
+                        continue
+                    with np.errstate(all="ignore"):
+                        m = s[r].max()
+                        p = np.exp(s[r] - m)
+                        o[b, h, r] = p @ v[b, g] / p.sum()
+                        lse[b, h, r] = m + np.log(p.sum())
+        return o, lse
+    return fn
+
+
+XMUTANTS = ["kv_head_mod", "offset_flip", "offset_ignored", "empty_rows_nan"]
+
+
+@pytest.mark.parametrize("kind", XMUTANTS)
+def test_grouped_shifted_pins_catch_planted_mistakes(kind):
+    fn = _xmutant(kind)
+    failed = []
+    for pin in XPINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(fn)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {kind!r}"
+
+
+def test_grouped_shifted_pins_accept_correct_copy():
+    fn = _xmutant("none")
+    for pin in XPINS:
+        pin(fn)
