@@ -27,12 +27,14 @@ FA_ERR_MISALIGNED = 8
 FA_ERR_ALIASING = 9
 FA_ERR_HIP = 10
 FA_ERR_WORKSPACE = 11
+FA_ERR_UNSUPPORTED_MASK = 12
 
 FA_LAYOUT_BNSD = 0
 FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
+FA_MASK_NONE, FA_MASK_CAUSAL_TOP_LEFT, FA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
-EXPORTS = ("fa_fwd", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size", "fa_status_str",
-           "fa_abi_version")
+EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+           "fa_status_str", "fa_abi_version")
 
 _lib = None
 
@@ -61,6 +63,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            vp]                            # stream
     lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_fwd_splitkv.argtypes = lib.fa_fwd.argtypes[:-1] + [ctypes.c_int, vp, i64, vp]
+    lib.fa_fwd_ex.restype = ctypes.c_int
+    lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                              ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                              ctypes.c_int, ctypes.c_int, vp, vp, vp,
+                              ctypes.c_int, vp, i64, vp]
     lib.fa_fwd_splitkv_workspace_size.restype = i64
     lib.fa_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -94,6 +101,15 @@ def fa_fwd_splitkv_raw(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, 
                                          workspace_size, stream)
 
 
+def fa_fwd_ex_raw(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask, keep_prob,
+                  in_dtype, o_dtype, descale_q, descale_k, descale_v, num_splits, workspace,
+                  workspace_size, stream) -> int:
+    """The general C entry point with integer pointers; returns the status code."""
+    return load_library().fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask,
+                                    keep_prob, in_dtype, o_dtype, descale_q, descale_k,
+                                    descale_v, num_splits, workspace, workspace_size, stream)
+
+
 def splitkv_workspace_size(B, H, Sq, Sk, D, causal=False, num_splits=0) -> int:
     """Workspace bytes fa_fwd_splitkv needs (0: a single range; -1: rejected sizes)."""
     return load_library().fa_fwd_splitkv_workspace_size(B, H, Sq, Sk, D, 1 if causal else 0,
@@ -123,14 +139,26 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
            descale_v=None, out=None, lse=None, stream=None):
     """Attention forward over BNSD tensors on the GPU.
 
-    q [B,H,Sq,D], k/v [B,H,Sk,D] contiguous GPU tensors (fp16, bf16 or
-    float8_e4m3fn). fp8 inputs need ``descale_*``: one-element fp32 GPU
+    q [B,H,Sq,D], k/v [B,H_kv,Sk,D] contiguous GPU tensors (fp16, bf16 or
+    float8_e4m3fn; H_kv divides H: query head h uses key/value head
+    h // (H / H_kv)). ``causal``: False, True (= "top_left": key j visible to
+    query i iff j <= i) or "bottom_right" (iff j <= i + Sk - Sq). fp8 inputs need ``descale_*``: one-element fp32 GPU
     tensors (value = code * descale). Returns (o, lse): o [B,H,Sq,D] in
     ``o_dtype`` (default: fp16 for fp16/fp8 inputs, bf16 for bf16 inputs),
     lse [B,H,Sq] fp32 (natural-log logsumexp of the scaled, masked scores).
     """
     return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
                  out, lse, stream, None, None)
+
+
+def _mask_code(causal) -> int:
+    if causal is False or causal is None:
+        return FA_MASK_NONE
+    if causal is True or causal == "top_left":
+        return FA_MASK_CAUSAL_TOP_LEFT
+    if causal == "bottom_right":
+        return FA_MASK_CAUSAL_BOTTOM_RIGHT
+    raise ValueError(f"causal must be False, True, 'top_left' or 'bottom_right', not {causal!r}")
 
 
 def fa_fwd_splitkv(q, k, v, *, num_splits: int = 0, scale: float | None = None,
@@ -156,9 +184,10 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, S, D]")
     B, H, Sq, D = q.shape
-    Sk = k.shape[2]
-    if tuple(k.shape) != (B, H, Sk, D) or tuple(v.shape) != (B, H, Sk, D):
-        raise ValueError("k and v must be [B, H, Sk, D] with q's B, H, D")
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, D) or tuple(v.shape) != (B, Hkv, Sk, D):
+        raise ValueError("k and v must be [B, H_kv, Sk, D] with q's B and D")
+    mask = _mask_code(causal)
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
     in_code = _dtype_code(q.dtype)
@@ -176,13 +205,15 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
     dv = descale_v.data_ptr() if descale_v is not None else None
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, H, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale), 1 if causal else 0,
-            float(keep_prob), in_code, _dtype_code(out.dtype), dq, dk, dv)
-    if num_splits is None:
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    tail = (float(keep_prob), in_code, _dtype_code(out.dtype), dq, dk, dv)
+    general = Hkv != H or mask == FA_MASK_CAUSAL_BOTTOM_RIGHT
+    args = ptrs + (B, H, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale), 1 if mask else 0) + tail
+    if num_splits is None and not general:
         _check_status(fa_fwd_raw(*args, stream))
         return out, lse
-    need = splitkv_workspace_size(B, H, Sq, Sk, D, causal, num_splits)
+    ns = 1 if num_splits is None else num_splits
+    need = splitkv_workspace_size(B, H, Sq, Sk, D, mask != FA_MASK_NONE, ns)
     if need < 0:
         raise ValueError("FA_ERR_BAD_SHAPE")
     if workspace is None and need > 0:
@@ -194,5 +225,9 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
         ws_size = workspace.numel() - (ws - base)
     else:
         ws, ws_size = None, 0
-    _check_status(fa_fwd_splitkv_raw(*args, num_splits, ws, ws_size, stream))
+    if general:
+        ex = ptrs + (B, H, Hkv, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale), mask) + tail
+        _check_status(fa_fwd_ex_raw(*ex, ns, ws, ws_size, stream))
+    else:
+        _check_status(fa_fwd_splitkv_raw(*args, ns, ws, ws_size, stream))
     return out, lse

@@ -72,6 +72,9 @@ struct Params {
   int64_t Sk;
   int32_t nqb;          // query blocks per (batch, head)
   int32_t total;        // B * H * nqb workgroups
+  int32_t H;            // query heads
+  int32_t Hkv;          // key/value heads (divides H; query head h uses h / (H / Hkv))
+  int64_t moff;         // causal: key j is visible to query i iff j <= i + moff
   float scale_log2;     // |scale| * log2(e)
   int32_t negate;       // scale < 0: Q fragments are negated (exact)
   // split-KV only: key-tile ranges per query block, partial results
@@ -319,15 +322,23 @@ struct FwdTile {
     Sq = p.Sq;
     Sk = p.Sk;
     q0 = (int64_t)qb * BM;
-    khead = p.k + (int64_t)bh * Sk * RB;
-    vhead = p.v + (int64_t)bh * Sk * RB;
+    {
+      const int b = bh / p.H;
+      const int kvh = (bh - b * p.H) / (p.H / p.Hkv);
+      const int64_t kvbh = (int64_t)b * p.Hkv + kvh;
+      khead = p.k + kvbh * Sk * RB;
+      vhead = p.v + kvbh * Sk * RB;
+    }
     qw0 = q0 + wave * 32;
     qrow = qw0 + l32;
     c = p.scale_log2;
     if constexpr (F8) c = fmaxf(c * (*p.descale_q) * (*p.descale_k), FLT_MIN);
 
     int64_t kend = Sk;
-    if constexpr (CAUSAL) kend = (q0 + BM) < Sk ? (q0 + BM) : Sk;
+    if constexpr (CAUSAL) {
+      kend = (q0 + BM + p.moff) < Sk ? (q0 + BM + p.moff) : Sk;
+      if (kend < 0) kend = 0;   // every row of the block lies above the diagonal
+    }
     ntiles = (int)((kend + BN - 1) / BN);
     jbeg = 0;
     if constexpr (SPLIT) {
@@ -340,7 +351,8 @@ struct FwdTile {
     }
     jlast = ntiles - 1;   // last tile this wave needs
     if constexpr (CAUSAL) {
-      const int64_t jl = (qw0 + 31) / BN;
+      const int64_t last_key = qw0 + 31 + p.moff;   // last key any row of this wave sees
+      const int64_t jl = last_key < 0 ? -1 : last_key / BN;
       jlast = jl < jlast ? (int)jl : jlast;
     }
     if (qw0 >= Sq) jlast = -1;   // all rows of this wave lie past Sq
@@ -540,7 +552,7 @@ struct FwdTile {
     // mask: keys past Sk, keys above the diagonal. key = kt0 + kb*32 +
     // 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or > this row's query:
     // compare the compile-time part with a per-lane limit.
-    const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > qw0);
+    const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > qw0 + p.moff);
     if (need_mask) {
       // keeps this a branch: full tiles (all but the last, or the diagonal
       // ones) then skip the compare-and-select on every score
@@ -548,7 +560,8 @@ struct FwdTile {
       const int64_t kv = Sk - kt0;
       int lim = kv < BN ? (int)kv : BN;
       if constexpr (CAUSAL) {
-        const int64_t qr = qrow - kt0 + 1;
+        int64_t qr = qrow + p.moff - kt0 + 1;
+        if (qr < 0) qr = 0;
         lim = qr < lim ? (int)qr : lim;
       }
       lim -= 4 * hl;
@@ -700,7 +713,10 @@ struct FwdTile {
       store_partial(l_tot);
       return;
     }
-    float inv_l = 1.f / l_tot;
+    // l = 0: the row sees no key (a diagonal shifted left of it); O = 0 and
+    // lse = -inf by definition
+    const bool any = l_tot > 0.f;
+    float inv_l = any ? 1.f / l_tot : 0.f;
     if constexpr (F8) inv_l *= *p.descale_v;
     if (qrow >= Sq) return;
     char* orow = p.o + ((int64_t)bh * Sq + qrow) * D * (OUT == OF32 ? 4 : 2);
@@ -722,7 +738,7 @@ struct FwdTile {
       }
     }
     if (hl == 0) {
-      p.lse[(int64_t)bh * Sq + qrow] = (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f;
+      p.lse[(int64_t)bh * Sq + qrow] = any ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
   }
 
@@ -752,8 +768,8 @@ struct FwdTile {
 };
 
 // ---- split-KV merge: for each row, lse = ln sum_s exp(lse_s) and
-// O = sum_s exp(lse_s - lse) * O_s over the nsplit ranges (every row sees
-// key 0 in some range, so at least one lse_s is finite). One lane per four
+// O = sum_s exp(lse_s - lse) * O_s over the nsplit ranges (a row whose
+// ranges all saw no key keeps O = 0, lse = -inf). One lane per four
 // head-dim entries of a row; memory-bound. ----
 struct MergeParams {
   const float* ws_o;
@@ -773,6 +789,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
   if (row >= p.rows) return;
   float m = -INFINITY;
   for (int s = 0; s < p.nsplit; ++s) m = fmaxf(m, p.ws_lse[(int64_t)s * p.rows + row]);
+  if (m == -INFINITY) m = 0.f;       // no key in any range: every weight below is 0
   float sum = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < p.nsplit; ++s) {
@@ -782,7 +799,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
     sum += w;
     acc += w * *(const f32x4*)(p.ws_o + r * D + d);
   }
-  const float inv = 1.f / sum;
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
   acc *= inv;
   if constexpr (OUT == OF32) {
     *(f32x4*)(p.o + (row * D + d) * 4) = acc;
@@ -790,7 +807,7 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
     constexpr int PK = (OUT == OBF16) ? KBF16 : KF16;
     *(u32x2*)(p.o + (row * D + d) * 2) = (u32x2){pack2<PK>(acc[0], acc[1]), pack2<PK>(acc[2], acc[3])};
   }
-  if (d == 0) p.lse[row] = m + logf(sum);
+  if (d == 0) p.lse[row] = sum > 0.f ? m + logf(sum) : -INFINITY;
 }
 
 // 32-key tiles in a ring of FA_NBUF buffers per tensor: 2 x 3 x 32 x D x 2
@@ -864,13 +881,17 @@ struct Call {
 };
 
 fa_status_t check_call(const void* q, const void* k, const void* v, void* o, float* lse,
-                       int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                       fa_layout_t layout, float scale, int causal, float keep_prob,
+                       int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Sk, int64_t D,
+                       fa_layout_t layout, float scale, fa_mask_t mask, float keep_prob,
                        fa_dtype_t in_dtype, fa_dtype_t o_dtype,
                        const float* descale_q, const float* descale_k, const float* descale_v,
                        Call& c) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL_POINTER;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return FA_ERR_BAD_SHAPE;
+  if (Hkv < 1 || Hkv > H || H % Hkv != 0 || H > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  if (mask != FA_MASK_NONE && mask != FA_MASK_CAUSAL_TOP_LEFT && mask != FA_MASK_CAUSAL_BOTTOM_RIGHT)
+    return FA_ERR_UNSUPPORTED_MASK;
+  const int causal = mask != FA_MASK_NONE;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED_HEAD_DIM;
   const bool ok_pair = (in_dtype == FA_F16 && (o_dtype == FA_F16 || o_dtype == FA_F32)) ||
                        (in_dtype == FA_BF16 && (o_dtype == FA_BF16 || o_dtype == FA_F32)) ||
@@ -899,7 +920,7 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
 
   const int64_t ie = dtype_size(in_dtype), oe = dtype_size(o_dtype);
   c.nq = BH * Sq * D * ie;
-  c.nk = BH * Sk * D * ie;
+  c.nk = B * Hkv * Sk * D * ie;
   c.no = BH * Sq * D * oe;
   c.nl = BH * Sq * 4;
   if (overlaps(o, c.no, q, c.nq) || overlaps(o, c.no, k, c.nk) || overlaps(o, c.no, v, c.nk) ||
@@ -928,6 +949,9 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
   p.nsplit = 1;
   p.ws_o = nullptr;
   p.ws_lse = nullptr;
+  p.H = (int32_t)H;
+  p.Hkv = (int32_t)Hkv;
+  p.moff = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT ? Sk - Sq : 0;
   c.nw = nw;
   c.BH = BH;
   c.nqb = nqb;
@@ -1001,47 +1025,21 @@ const char* fa_status_str(fa_status_t s) {
     case FA_ERR_ALIASING: return "FA_ERR_ALIASING";
     case FA_ERR_HIP: return "FA_ERR_HIP";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_UNSUPPORTED_MASK: return "FA_ERR_UNSUPPORTED_MASK";
   }
   return "FA_ERR_UNKNOWN";
 }
 
-fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                   fa_layout_t layout, float scale, int causal, float keep_prob,
-                   fa_dtype_t in_dtype, fa_dtype_t o_dtype,
-                   const float* descale_q, const float* descale_k, const float* descale_v,
-                   hipStream_t stream) {
+fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
+                      fa_layout_t layout, float scale, fa_mask_t mask, float keep_prob,
+                      fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                      const float* descale_q, const float* descale_k, const float* descale_v,
+                      int num_splits, void* workspace, int64_t workspace_size,
+                      hipStream_t stream) {
   Call c;
-  const fa_status_t st = check_call(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_prob,
-                                    in_dtype, o_dtype, descale_q, descale_k, descale_v, c);
-  if (st != FA_OK) return st;
-  hipLaunchKernelGGL(pick_kernel<false>(c), dim3((unsigned)c.p.total), dim3(64 * c.nw), 0, stream, c.p);
-  if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
-  return FA_OK;
-}
-
-int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                                      int causal, int num_splits) {
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || (D != 64 && D != 128)) return -1;
-  if (num_splits < 0 || num_splits > kMaxSplits) return -1;
-  const int64_t lim = (int64_t)1 << 40;
-  if (B > lim / H || Sq > lim || Sk > lim || B * H > lim / Sq || B * H > lim / Sk) return -1;
-  const int nw = fa::waves_for((int)D, causal != 0);
-  const int64_t nqb = (Sq + 32 * nw - 1) / (32 * nw);
-  const int ns = num_splits ? num_splits : auto_splits(B * H, nqb, Sk, nw);
-  return workspace_bytes(B * H, Sq, D, ns);
-}
-
-fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
-                           fa_layout_t layout, float scale, int causal, float keep_prob,
-                           fa_dtype_t in_dtype, fa_dtype_t o_dtype,
-                           const float* descale_q, const float* descale_k, const float* descale_v,
-                           int num_splits, void* workspace, int64_t workspace_size,
-                           hipStream_t stream) {
-  Call c;
-  const fa_status_t st = check_call(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_prob,
-                                    in_dtype, o_dtype, descale_q, descale_k, descale_v, c);
+  const fa_status_t st = check_call(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask,
+                                    keep_prob, in_dtype, o_dtype, descale_q, descale_k, descale_v, c);
   if (st != FA_OK) return st;
   if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_BAD_SHAPE;
   const int ns = num_splits ? num_splits : auto_splits(c.BH, c.nqb, Sk, c.nw);
@@ -1079,6 +1077,41 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   hipLaunchKernelGGL(pick_merge(c), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, m);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   return FA_OK;
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                   fa_layout_t layout, float scale, int causal, float keep_prob,
+                   fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                   const float* descale_q, const float* descale_k, const float* descale_v,
+                   hipStream_t stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, Sq, Sk, D, layout, scale,
+                   causal ? FA_MASK_CAUSAL_TOP_LEFT : FA_MASK_NONE, keep_prob, in_dtype, o_dtype,
+                   descale_q, descale_k, descale_v, 1, nullptr, 0, stream);
+}
+
+int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                      int causal, int num_splits) {
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || (D != 64 && D != 128)) return -1;
+  if (num_splits < 0 || num_splits > kMaxSplits) return -1;
+  const int64_t lim = (int64_t)1 << 40;
+  if (B > lim / H || Sq > lim || Sk > lim || B * H > lim / Sq || B * H > lim / Sk) return -1;
+  const int nw = fa::waves_for((int)D, causal != 0);
+  const int64_t nqb = (Sq + 32 * nw - 1) / (32 * nw);
+  const int ns = num_splits ? num_splits : auto_splits(B * H, nqb, Sk, nw);
+  return workspace_bytes(B * H, Sq, D, ns);
+}
+
+fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                           fa_layout_t layout, float scale, int causal, float keep_prob,
+                           fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                           const float* descale_q, const float* descale_k, const float* descale_v,
+                           int num_splits, void* workspace, int64_t workspace_size,
+                           hipStream_t stream) {
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, Sq, Sk, D, layout, scale,
+                   causal ? FA_MASK_CAUSAL_TOP_LEFT : FA_MASK_NONE, keep_prob, in_dtype, o_dtype,
+                   descale_q, descale_k, descale_v, num_splits, workspace, workspace_size, stream);
 }
 
 }  // extern "C"

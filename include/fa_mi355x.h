@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 2
+#define FA_ABI_VERSION 3
 
 typedef enum {
   FA_OK = 0,
@@ -70,12 +70,21 @@ typedef enum {
   FA_ERR_MISALIGNED = 8,           /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   FA_ERR_ALIASING = 9,             /* o or lse overlaps q, k, v, or each other */
   FA_ERR_HIP = 10,                 /* a kernel launch failed */
-  FA_ERR_WORKSPACE = 11            /* fa_fwd_splitkv: workspace NULL or smaller than needed */
+  FA_ERR_WORKSPACE = 11,           /* split-KV: workspace NULL or smaller than needed */
+  FA_ERR_UNSUPPORTED_MASK = 12     /* fa_fwd_ex: mask not one of fa_mask_t */
 } fa_status_t;
 
 typedef enum { FA_LAYOUT_BNSD = 0 } fa_layout_t;
 
 typedef enum { FA_F16 = 0, FA_BF16 = 1, FA_FP8_E4M3 = 2, FA_F32 = 3 } fa_dtype_t;
+
+/* Causal masks. TOP_LEFT: key j visible to query i iff j <= i (the
+ * verifier's upper-triangle mask in "ops-transformer FlashAttention on
+ * Ascend: build, run and tune", section 4.3; every row sees key 0).
+ * BOTTOM_RIGHT: iff j <= i + (Sk - Sq), the diagonal through the last query
+ * and the last key (the same as TOP_LEFT when Sq == Sk); with Sq > Sk the
+ * first Sq - Sk rows see no key and get O = 0, lse = -inf. */
+typedef enum { FA_MASK_NONE = 0, FA_MASK_CAUSAL_TOP_LEFT = 1, FA_MASK_CAUSAL_BOTTOM_RIGHT = 2 } fa_mask_t;
 
 /*
  * fa_fwd — attention forward on one GPU.
@@ -138,6 +147,34 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
  */
 int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                                       int causal, int num_splits);
+
+/*
+ * fa_fwd_ex — the general entry point behind fa_fwd and fa_fwd_splitkv:
+ * grouped key/value heads, the causal mask alignment, and the split-KV
+ * arguments.
+ *
+ * k, v: [B, H_kv, Sk, D] with H_kv dividing H; query head h attends to
+ *   key/value head h / (H / H_kv) (H_kv = H: one each; H_kv = 1: one shared
+ *   head). Layout of k, v: ((b*H_kv+g)*Sk+s)*D+d.
+ * mask: one of fa_mask_t (FA_ERR_UNSUPPORTED_MASK otherwise).
+ * num_splits, workspace, workspace_size: as fa_fwd_splitkv (num_splits = 1
+ *   and a NULL workspace give one kernel, as fa_fwd); the workspace size
+ *   comes from fa_fwd_splitkv_workspace_size(B, H, Sq, Sk, D, mask != 0,
+ *   num_splits).
+ * Other arguments, ownership and errors as fa_fwd; H_kv < 1, H_kv > H or
+ * H % H_kv != 0 is FA_ERR_BAD_SHAPE. The variants come from the survey of
+ * the pages' call (the npu_flash_attention call has head_num and a layout;
+ * grouped heads and the bottom-right diagonal are the pages' Sq != Sk and
+ * layout-contract lessons, "Hygon FlashAttention: fixed-defect review",
+ * item 12).
+ */
+fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
+                      fa_layout_t layout, float scale, fa_mask_t mask, float keep_prob,
+                      fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                      const float* descale_q, const float* descale_k, const float* descale_v,
+                      int num_splits, void* workspace, int64_t workspace_size,
+                      hipStream_t stream);
 
 /* Human-readable name of a status code ("FA_OK", ...); never NULL. */
 const char* fa_status_str(fa_status_t s);

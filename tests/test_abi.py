@@ -41,10 +41,11 @@ def test_library_holds_gfx950_code():
 
 def test_abi_version_and_status_strings():
     lib = fa.load_library()
-    assert lib.fa_abi_version() == 2
-    names = [fa.status_str(c) for c in range(12)]
+    assert lib.fa_abi_version() == 3
+    names = [fa.status_str(c) for c in range(13)]
     assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP" and names[11] == "FA_ERR_WORKSPACE"
-    assert len(set(names)) == 12
+    assert names[12] == "FA_ERR_UNSUPPORTED_MASK"
+    assert len(set(names)) == 13
     assert fa.status_str(99) == "FA_ERR_UNKNOWN"
 
 
@@ -148,3 +149,37 @@ def test_splitkv_workspace_size():
 ])
 def test_splitkv_rejects_before_launch(over, code):
     assert call_split(**over) == code
+
+
+# ---- the general entry point ----
+def call_ex(**over):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=8, H_kv=2, Sq=64, Sk=64, D=128,
+             layout=fa.FA_LAYOUT_BNSD, scale=0.125, mask=fa.FA_MASK_CAUSAL_BOTTOM_RIGHT,
+             keep_prob=1.0, in_dtype=fa.FA_F16, o_dtype=fa.FA_F16, descale_q=None,
+             descale_k=None, descale_v=None, num_splits=1, workspace=None, workspace_size=0,
+             stream=None)
+    a.update(over)
+    return fa.fa_fwd_ex_raw(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(H_kv=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(H_kv=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(H_kv=16), fa.FA_ERR_BAD_SHAPE),
+    (dict(mask=3), fa.FA_ERR_UNSUPPORTED_MASK),
+    (dict(mask=-1), fa.FA_ERR_UNSUPPORTED_MASK),
+    (dict(num_splits=4), fa.FA_ERR_WORKSPACE),
+    (dict(v=None), fa.FA_ERR_NULL_POINTER),
+    # k of H_kv heads ends before o starts: o right after k is no alias,
+    # o inside k's H_kv-head extent is
+    (dict(o=K + 2 * 64 * 128 * 2 - 256), fa.FA_ERR_ALIASING),
+])
+def test_ex_rejects_before_launch(over, code):
+    assert call_ex(**over) == code
+
+
+def test_python_wrapper_rejects_unknown_mask():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa._mask_code("diagonal")

@@ -1,0 +1,68 @@
+"""GPU parity of grouped key/value heads (k, v with H_kv heads) and the
+bottom-right causal alignment against the fp64 oracle, through the C ABI
+(fa_fwd_ex; the plain and the split-KV paths)."""
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_07_amd as fa
+import fa_inputs as fi
+from oracle import attention_fp64
+from parity_util import compare
+
+pytestmark = pytest.mark.gpu
+
+MASKS = {"none": (False, 0), "top_left": (True, 0), "bottom_right": (True, None)}
+
+
+def run_case(dtype, D, H, Hkv, Sq, Sk, mask, num_splits, seed):
+    cfg = fi.Config("gqa", 2, H, Sq, Sk, D, dtype, MASKS[mask][0], seed=seed)
+    inp = fi.make_inputs(cfg)
+    # the first H_kv heads of the drawn k, v are the grouped key/value heads
+    inp.k = inp.k[:, :Hkv].contiguous()
+    inp.v = inp.v[:, :Hkv].contiguous()
+    q64, k64, v64 = fi.values(inp)
+    offset = (Sk - Sq) if mask == "bottom_right" else 0
+    ref_o, ref_l = attention_fp64(q64, k64, v64, cfg.scale, MASKS[mask][0], offset)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    kw = {}
+    if dtype == fi.FP8:
+        kw = {n: torch.tensor([d], dtype=torch.float32, device="cuda") for n, d in
+              (("descale_q", inp.descale_q), ("descale_k", inp.descale_k),
+               ("descale_v", inp.descale_v))}
+    causal = False if mask == "none" else mask
+    native = fi.BF16 if dtype == fi.BF16 else fi.F16
+    for od in (fi.F32, native):
+        if num_splits is None:
+            o, lse = fa.fa_fwd(q, k, v, scale=cfg.scale, causal=causal,
+                               o_dtype=fi.TORCH_DTYPE[od], **kw)
+        else:
+            o, lse = fa.fa_fwd_splitkv(q, k, v, num_splits=num_splits, scale=cfg.scale,
+                                       causal=causal, o_dtype=fi.TORCH_DTYPE[od], **kw)
+        torch.cuda.synchronize()
+        o = o.double().cpu().numpy()
+        lse = lse.double().cpu().numpy()
+        what = f"{dtype} D{D} H{H}/{Hkv} {Sq}x{Sk} {mask} splits {num_splits} {od}"
+        empty = np.isneginf(ref_l)
+        # rows without a visible key: O = 0 and lse = -inf exactly
+        assert np.all(np.isneginf(lse[empty])), what
+        assert np.all(o[empty] == 0.0), what
+        assert not np.any(np.isneginf(lse[~empty])), what
+        compare(cfg, od, o[~empty], lse[~empty], ref_o[~empty], ref_l[~empty], what=what)
+
+
+@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16, fi.FP8])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_grouped_heads_and_masks(dtype, D, mask):
+    for i, (H, Hkv, Sq, Sk) in enumerate([(4, 1, 65, 130), (6, 2, 130, 65), (4, 4, 1, 200),
+                                          (4, 2, 200, 1), (2, 1, 257, 300)]):
+        for ns in (None, 3):
+            run_case(dtype, D, H, Hkv, Sq, Sk, mask, ns, seed=900 + 10 * i)
+
+
+def test_bottom_right_long_tail_of_empty_rows():
+    """Sq far above Sk: all but the last Sk rows see no key (whole blocks of
+    empty rows, and blocks whose waves are partly empty)."""
+    run_case(fi.F16, 128, 4, 2, 1000, 70, "bottom_right", None, seed=990)
+    run_case(fi.F16, 64, 4, 2, 1000, 70, "bottom_right", 4, seed=991)
