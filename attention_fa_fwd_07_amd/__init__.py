@@ -30,6 +30,7 @@ FA_ERR_WORKSPACE = 11
 FA_ERR_UNSUPPORTED_MASK = 12
 
 FA_LAYOUT_BNSD = 0
+FA_LAYOUT_BSHD = 1
 FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL_TOP_LEFT, FA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
@@ -136,19 +137,21 @@ def _check_status(code: int) -> None:
 
 def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
            keep_prob: float = 1.0, o_dtype=None, descale_q=None, descale_k=None,
-           descale_v=None, out=None, lse=None, stream=None):
+           descale_v=None, out=None, lse=None, stream=None, layout: str = "BNSD"):
     """Attention forward over BNSD tensors on the GPU.
 
     q [B,H,Sq,D], k/v [B,H_kv,Sk,D] contiguous GPU tensors (fp16, bf16 or
     float8_e4m3fn; H_kv divides H: query head h uses key/value head
     h // (H / H_kv)). ``causal``: False, True (= "top_left": key j visible to
-    query i iff j <= i) or "bottom_right" (iff j <= i + Sk - Sq). fp8 inputs need ``descale_*``: one-element fp32 GPU
+    query i iff j <= i) or "bottom_right" (iff j <= i + Sk - Sq).
+    ``layout="BSHD"``: q, o [B,Sq,H,D] and k, v [B,Sk,H_kv,D] instead (lse
+    stays [B,H,Sq]). fp8 inputs need ``descale_*``: one-element fp32 GPU
     tensors (value = code * descale). Returns (o, lse): o [B,H,Sq,D] in
     ``o_dtype`` (default: fp16 for fp16/fp8 inputs, bf16 for bf16 inputs),
     lse [B,H,Sq] fp32 (natural-log logsumexp of the scaled, masked scores).
     """
     return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
-                 out, lse, stream, None, None)
+                 out, lse, stream, None, None, layout)
 
 
 def _mask_code(causal) -> int:
@@ -164,17 +167,17 @@ def _mask_code(causal) -> int:
 def fa_fwd_splitkv(q, k, v, *, num_splits: int = 0, scale: float | None = None,
                    causal: bool = False, keep_prob: float = 1.0, o_dtype=None, descale_q=None,
                    descale_k=None, descale_v=None, out=None, lse=None, workspace=None,
-                   stream=None):
+                   stream=None, layout: str = "BNSD"):
     """fa_fwd with the keys of each query block split into ``num_splits``
     ranges (0: chosen to fill the GPU), merged by logsumexp. ``workspace``:
     an optional uint8 GPU tensor of at least ``splitkv_workspace_size(...)``
     bytes (allocated here when not given)."""
     return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
-                 out, lse, stream, int(num_splits), workspace)
+                 out, lse, stream, int(num_splits), workspace, layout)
 
 
 def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
-          out, lse, stream, num_splits, workspace):
+          out, lse, stream, num_splits, workspace, layout="BNSD"):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -183,10 +186,20 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
             raise ValueError(f"{name} must be contiguous (BNSD)")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, S, D]")
-    B, H, Sq, D = q.shape
-    Hkv, Sk = k.shape[1], k.shape[2]
-    if tuple(k.shape) != (B, Hkv, Sk, D) or tuple(v.shape) != (B, Hkv, Sk, D):
-        raise ValueError("k and v must be [B, H_kv, Sk, D] with q's B and D")
+    if layout == "BNSD":
+        lay = FA_LAYOUT_BNSD
+        B, H, Sq, D = q.shape
+        Hkv, Sk = k.shape[1], k.shape[2]
+        kv_shape = (B, Hkv, Sk, D)
+    elif layout == "BSHD":
+        lay = FA_LAYOUT_BSHD
+        B, Sq, H, D = q.shape
+        Sk, Hkv = k.shape[1], k.shape[2]
+        kv_shape = (B, Sk, Hkv, D)
+    else:
+        raise ValueError(f"layout must be 'BNSD' or 'BSHD', not {layout!r}")
+    if tuple(k.shape) != kv_shape or tuple(v.shape) != kv_shape:
+        raise ValueError(f"k and v must be {layout} with q's B and D")
     mask = _mask_code(causal)
     if not (q.dtype == k.dtype == v.dtype):
         raise ValueError("q, k, v must share a dtype")
@@ -197,7 +210,7 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
         scale = 1.0 / math.sqrt(D)
     dev = q.device
     if out is None:
-        out = torch.empty((B, H, Sq, D), dtype=o_dtype, device=dev)
+        out = torch.empty(tuple(q.shape), dtype=o_dtype, device=dev)
     if lse is None:
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=dev)
     dq = descale_q.data_ptr() if descale_q is not None else None
@@ -207,7 +220,7 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
         stream = torch.cuda.current_stream(dev).cuda_stream
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
     tail = (float(keep_prob), in_code, _dtype_code(out.dtype), dq, dk, dv)
-    general = Hkv != H or mask == FA_MASK_CAUSAL_BOTTOM_RIGHT
+    general = Hkv != H or mask == FA_MASK_CAUSAL_BOTTOM_RIGHT or lay != FA_LAYOUT_BNSD
     args = ptrs + (B, H, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale), 1 if mask else 0) + tail
     if num_splits is None and not general:
         _check_status(fa_fwd_raw(*args, stream))
@@ -226,7 +239,7 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
     else:
         ws, ws_size = None, 0
     if general:
-        ex = ptrs + (B, H, Hkv, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale), mask) + tail
+        ex = ptrs + (B, H, Hkv, Sq, Sk, D, lay, float(scale), mask) + tail
         _check_status(fa_fwd_ex_raw(*ex, ns, ws, ws_size, stream))
     else:
         _check_status(fa_fwd_splitkv_raw(*args, ns, ws, ws_size, stream))

@@ -74,6 +74,10 @@ struct Params {
   int32_t total;        // B * H * nqb workgroups
   int32_t H;            // query heads
   int32_t Hkv;          // key/value heads (divides H; query head h uses h / (H / Hkv))
+  // element strides of (batch, head, row): q and o share theirs, k and v
+  // theirs (BNSD: H*S*D, S*D, D; BSHD: S*H*D, D, H*D); rows are contiguous
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
   int64_t moff;         // causal: key j is visible to query i iff j <= i + moff
   float scale_log2;     // |scale| * log2(e)
   int32_t negate;       // scale < 0: Q fragments are negated (exact)
@@ -294,6 +298,8 @@ struct FwdTile {
   int64_t Sq, Sk, q0, qw0, qrow;
   const char* khead;
   const char* vhead;
+  int kpitch;                       // bytes from one K/V row to the next in HBM
+  int64_t qbase;                    // element offset of this (batch, head) in q and o
   float c;                          // softmax scale in log2 units (fp8: times dq * dk)
 
   qfrag_t qf[NDS];
@@ -324,10 +330,13 @@ struct FwdTile {
     q0 = (int64_t)qb * BM;
     {
       const int b = bh / p.H;
-      const int kvh = (bh - b * p.H) / (p.H / p.Hkv);
-      const int64_t kvbh = (int64_t)b * p.Hkv + kvh;
-      khead = p.k + kvbh * Sk * RB;
-      vhead = p.v + kvbh * Sk * RB;
+      const int h = bh - b * p.H;
+      const int kvh = h / (p.H / p.Hkv);
+      const int64_t koff = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+      khead = p.k + koff * ES;
+      vhead = p.v + koff * ES;
+      kpitch = (int)(p.k_ss * ES);
+      qbase = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
     }
     qw0 = q0 + wave * 32;
     qrow = qw0 + l32;
@@ -360,7 +369,7 @@ struct FwdTile {
     // Q fragments (B operand of S^T = K Q^T), kept in registers; rows past
     // Sq read the last row (their results are never stored). Negative
     // scales negate Q (exact).
-    const char* qrowp = p.q + ((int64_t)bh * Sq + (qrow < Sq ? qrow : Sq - 1)) * RB;
+    const char* qrowp = p.q + (qbase + (qrow < Sq ? qrow : Sq - 1) * p.q_ss) * ES;
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       if constexpr (F8) {
@@ -418,8 +427,8 @@ struct FwdTile {
     {
       const int r = (tid & (NT - 1)) / C;
       const int pc = tid % C;
-      goff_k = (uint32_t)(r * RB + ((pc ^ swz_k<RB>(r)) << 4));
-      goff_v = (uint32_t)(r * RB + ((pc ^ swz_v<RB, F8>(r)) << 4));
+      goff_k = (uint32_t)(r * kpitch + ((pc ^ swz_k<RB>(r)) << 4));
+      goff_v = (uint32_t)(r * kpitch + ((pc ^ swz_v<RB, F8>(r)) << 4));
     }
 
 #pragma unroll
@@ -434,13 +443,13 @@ struct FwdTile {
   __device__ __forceinline__ void load_one(int j, int buf) {
     if (wave >= LWAVES) return;   // only the first LWAVES waves issue loads
     const int64_t row0 = (int64_t)j * BN;
-    const char* base = (IS_V ? vhead : khead) + row0 * RB;
+    const char* base = (IS_V ? vhead : khead) + row0 * kpitch;
     const uint32_t dst = lds0 + (IS_V ? NB + buf : buf) * TILE + wave * 64 * 16;
     const uint32_t goff = IS_V ? goff_v : goff_k;
     const int64_t left = Sk - 1 - row0;
     if (left >= BN - 1) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) dma16(base + i * (NT / C) * RB, goff, dst + i * NT * 16);
+      for (int i = 0; i < LOADS; ++i) dma16(base + (int64_t)i * (NT / C) * kpitch, goff, dst + i * NT * 16);
     } else {
       const int rmax = (int)left;
 #pragma unroll
@@ -450,7 +459,7 @@ struct FwdTile {
         const int pc = pidx % C;
         const int rr = r < rmax ? r : rmax;
         const int sw = IS_V ? swz_v<RB, F8>(r) : swz_k<RB>(r);
-        dma16(base, (uint32_t)(rr * RB + ((pc ^ sw) << 4)), dst + i * NT * 16);
+        dma16(base, (uint32_t)(rr * kpitch + ((pc ^ sw) << 4)), dst + i * NT * 16);
       }
     }
   }
@@ -719,7 +728,7 @@ struct FwdTile {
     float inv_l = any ? 1.f / l_tot : 0.f;
     if constexpr (F8) inv_l *= *p.descale_v;
     if (qrow >= Sq) return;
-    char* orow = p.o + ((int64_t)bh * Sq + qrow) * D * (OUT == OF32 ? 4 : 2);
+    char* orow = p.o + (qbase + qrow * p.q_ss) * (OUT == OF32 ? 4 : 2);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -776,8 +785,11 @@ struct MergeParams {
   const float* ws_lse;
   char* o;
   float* lse;
-  int64_t rows;         // B*H*Sq
+  int64_t rows;         // B*H*Sq, in (batch, head, row) order
   int32_t nsplit;
+  int32_t H;
+  int64_t Sq;
+  int64_t q_sb, q_sh, q_ss;   // element strides of o (as Params)
 };
 
 template <int D, int OUT>
@@ -801,11 +813,14 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
   }
   const float inv = sum > 0.f ? 1.f / sum : 0.f;
   acc *= inv;
+  const int64_t bh = row / p.Sq, srow = row - bh * p.Sq;
+  const int64_t b = bh / p.H, h = bh - b * p.H;
+  const int64_t oel = b * p.q_sb + h * p.q_sh + srow * p.q_ss + d;
   if constexpr (OUT == OF32) {
-    *(f32x4*)(p.o + (row * D + d) * 4) = acc;
+    *(f32x4*)(p.o + oel * 4) = acc;
   } else {
     constexpr int PK = (OUT == OBF16) ? KBF16 : KF16;
-    *(u32x2*)(p.o + (row * D + d) * 2) = (u32x2){pack2<PK>(acc[0], acc[1]), pack2<PK>(acc[2], acc[3])};
+    *(u32x2*)(p.o + oel * 2) = (u32x2){pack2<PK>(acc[0], acc[1]), pack2<PK>(acc[2], acc[3])};
   }
   if (d == 0) p.lse[row] = sum > 0.f ? m + logf(sum) : -INFINITY;
 }
@@ -901,7 +916,7 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
     if (!descale_q || !descale_k || !descale_v) return FA_ERR_NULL_POINTER;
     if (((uintptr_t)descale_q | (uintptr_t)descale_k | (uintptr_t)descale_v) & 3) return FA_ERR_MISALIGNED;
   }
-  if (layout != FA_LAYOUT_BNSD) return FA_ERR_UNSUPPORTED_LAYOUT;
+  if (layout != FA_LAYOUT_BNSD && layout != FA_LAYOUT_BSHD) return FA_ERR_UNSUPPORTED_LAYOUT;
   if (keep_prob != 1.0f) return FA_ERR_UNSUPPORTED_DROPOUT;
   if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
 
@@ -951,6 +966,15 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
   p.ws_lse = nullptr;
   p.H = (int32_t)H;
   p.Hkv = (int32_t)Hkv;
+  if (layout == FA_LAYOUT_BNSD) {
+    p.q_sb = H * Sq * D; p.q_sh = Sq * D; p.q_ss = D;
+    p.k_sb = Hkv * Sk * D; p.k_sh = Sk * D; p.k_ss = D;
+  } else {   // BSHD
+    p.q_sb = Sq * H * D; p.q_sh = D; p.q_ss = H * D;
+    p.k_sb = Sk * Hkv * D; p.k_sh = D; p.k_ss = Hkv * D;
+  }
+  // one K/V row pitch in bytes must fit the 32-bit per-lane load offsets
+  if (p.k_ss * ie * 32 > INT32_MAX) return FA_ERR_BAD_SHAPE;
   p.moff = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT ? Sk - Sq : 0;
   c.nw = nw;
   c.BH = BH;
@@ -1073,6 +1097,11 @@ fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, floa
   m.lse = lse;
   m.rows = c.BH * Sq;
   m.nsplit = ns;
+  m.H = (int32_t)H;
+  m.Sq = Sq;
+  m.q_sb = c.p.q_sb;
+  m.q_sh = c.p.q_sh;
+  m.q_ss = c.p.q_ss;
   const int64_t lanes = m.rows * (D / 4);
   hipLaunchKernelGGL(pick_merge(c), dim3((unsigned)((lanes + 255) / 256)), dim3(256), 0, stream, m);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;

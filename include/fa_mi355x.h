@@ -23,9 +23,10 @@
  * 1.2). The per-row logsumexp output is not defined on the pages; it is the
  * natural-log logsumexp of the scaled, masked score row.
  *
- * Layout: contiguous BNSD. q and o: element (b,h,s,d) at ((b*H+h)*Sq+s)*D+d;
- * k and v: ((b*H+h)*Sk+s)*D+d; lse: fp32 [B,H,Sq] at (b*H+h)*Sq+s. All
- * offsets are computed in 64-bit integers.
+ * Layout: contiguous BNSD (fa_fwd_ex also takes BSHD, see fa_layout_t). q
+ * and o: element (b,h,s,d) at ((b*H+h)*Sq+s)*D+d; k and v:
+ * ((b*H+h)*Sk+s)*D+d; lse: fp32 [B,H,Sq] at (b*H+h)*Sq+s. All offsets are
+ * computed in 64-bit integers.
  *
  * Supported (in_dtype -> o_dtype): F16 -> {F16, F32}; BF16 -> {BF16, F32};
  * FP8_E4M3 -> {F16, F32}. Head dim D in {64, 128}. FP8_E4M3 is OCP e4m3fn;
@@ -74,7 +75,11 @@ typedef enum {
   FA_ERR_UNSUPPORTED_MASK = 12     /* fa_fwd_ex: mask not one of fa_mask_t */
 } fa_status_t;
 
-typedef enum { FA_LAYOUT_BNSD = 0 } fa_layout_t;
+/* Memory layouts of q, k, v and o (contiguous): BNSD = [B, heads, S, D];
+ * BSHD = [B, S, heads, D] (the sequence-major [B, S, H*D] tensors of the
+ * first page's data generator and verifier, section 4, with the hidden
+ * size split into heads). lse is [B, H, Sq] fp32 in either layout. */
+typedef enum { FA_LAYOUT_BNSD = 0, FA_LAYOUT_BSHD = 1 } fa_layout_t;
 
 typedef enum { FA_F16 = 0, FA_BF16 = 1, FA_FP8_E4M3 = 2, FA_F32 = 3 } fa_dtype_t;
 

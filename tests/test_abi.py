@@ -84,7 +84,7 @@ def call(**over):
     (dict(in_dtype=fa.FA_FP8_E4M3, o_dtype=fa.FA_F16), fa.FA_ERR_NULL_POINTER),
     (dict(in_dtype=fa.FA_FP8_E4M3, o_dtype=fa.FA_BF16, descale_q=DQ, descale_k=DK,
           descale_v=DV), fa.FA_ERR_UNSUPPORTED_DTYPE),
-    (dict(layout=1), fa.FA_ERR_UNSUPPORTED_LAYOUT),
+    (dict(layout=2), fa.FA_ERR_UNSUPPORTED_LAYOUT),
     (dict(keep_prob=0.9), fa.FA_ERR_UNSUPPORTED_DROPOUT),
     (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
     (dict(scale=float("inf")), fa.FA_ERR_BAD_SCALE),

@@ -66,3 +66,41 @@ def test_bottom_right_long_tail_of_empty_rows():
     empty rows, and blocks whose waves are partly empty)."""
     run_case(fi.F16, 128, 4, 2, 1000, 70, "bottom_right", None, seed=990)
     run_case(fi.F16, 64, 4, 2, 1000, 70, "bottom_right", 4, seed=991)
+
+
+@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16, fi.FP8])
+@pytest.mark.parametrize("D", [64, 128])
+def test_bshd_layout(dtype, D):
+    """q, o [B,Sq,H,D] and k, v [B,Sk,H_kv,D]: the BNSD inputs, transposed;
+    the result transposed back must match the oracle."""
+    for i, (H, Hkv, Sq, Sk, mask, ns) in enumerate([
+            (4, 2, 100, 300, "none", None), (6, 3, 257, 257, "top_left", None),
+            (4, 1, 300, 100, "bottom_right", None), (4, 4, 129, 700, "top_left", 3)]):
+        cfg = fi.Config("bshd", 2, H, Sq, Sk, D, dtype, mask != "none", seed=960 + i)
+        inp = fi.make_inputs(cfg)
+        inp.k = inp.k[:, :Hkv].contiguous()
+        inp.v = inp.v[:, :Hkv].contiguous()
+        q64, k64, v64 = fi.values(inp)
+        offset = (Sk - Sq) if mask == "bottom_right" else 0
+        ref_o, ref_l = attention_fp64(q64, k64, v64, cfg.scale, mask != "none", offset)
+        q, k, v = (t.transpose(1, 2).contiguous().cuda() for t in (inp.q, inp.k, inp.v))
+        kw = {}
+        if dtype == fi.FP8:
+            kw = {n: torch.tensor([d], dtype=torch.float32, device="cuda") for n, d in
+                  (("descale_q", inp.descale_q), ("descale_k", inp.descale_k),
+                   ("descale_v", inp.descale_v))}
+        causal = False if mask == "none" else mask
+        if ns is None:
+            o, lse = fa.fa_fwd(q, k, v, scale=cfg.scale, causal=causal, layout="BSHD",
+                               o_dtype=torch.float32, **kw)
+        else:
+            o, lse = fa.fa_fwd_splitkv(q, k, v, num_splits=ns, scale=cfg.scale, causal=causal,
+                                       layout="BSHD", o_dtype=torch.float32, **kw)
+        torch.cuda.synchronize()
+        assert tuple(o.shape) == (2, Sq, H, D) and tuple(lse.shape) == (2, H, Sq)
+        o = o.transpose(1, 2).double().cpu().numpy()
+        lse = lse.double().cpu().numpy()
+        empty = np.isneginf(ref_l)
+        assert np.all(o[empty] == 0.0) and np.all(np.isneginf(lse[empty]))
+        compare(cfg, fi.F32, o[~empty], lse[~empty], ref_o[~empty], ref_l[~empty],
+                what=f"BSHD {dtype} D{D} H{H}/{Hkv} {Sq}x{Sk} {mask} splits {ns}")
