@@ -21,6 +21,15 @@ that FlashAttention reaches exactly, up to rounding order:
   * grouped key/value heads: k and v may have H_kv heads with H_kv dividing
     the query head count H; query head h then attends to key/value head
     h // (H / H_kv) (H_kv = 1 shares one key/value head among all);
+  * variable-length batches ("Hygon FlashAttention: fixed-defect review",
+    chatdocs.ruinique.com/hygon/flash-attention-fixed-bugs, item 17, the
+    varlen forward whose packed token offsets outgrow 32 bits): the pages
+    name the packed form but do not define it. The reading adopted: the B
+    sequences are stored one after another along the token axis, sequence
+    b owning query rows cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] ..
+    cu_k[b+1]-1, and each is an attention problem of its own (no query sees
+    another sequence's keys), its causal diagonal placed inside the
+    sequence. A sequence with no key has only rows without a visible key;
   * P = softmax(S) along the key axis, computed the safe way: subtract the
     row maximum before exponentiating (same page, section 6.2, the
     numerically stable softmax and its second, normalising pass);
@@ -69,6 +78,10 @@ def head_forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     idx = np.arange(q.shape[0]) if rows is None else np.asarray(rows, np.int64)
+    if k.shape[0] == 0:                                            # no key at all: every
+        o = np.zeros((len(idx), v.shape[1]))                       # row is without a
+        lse = np.full(len(idx), -np.inf)                           # visible key
+        return (o, lse, np.zeros((len(idx), 0))) if return_p else (o, lse)
     s = (q[idx] @ k.T) * np.float64(scale)                       # S = scale*QK^T
     if causal:
         key = np.arange(k.shape[0])
@@ -101,6 +114,38 @@ def attention_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
             kv = h // group
             o[b, h], lse[b, h] = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal,
                                               offset=offset)
+    return o, lse
+
+
+def attention_varlen_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k,
+                          scale: float, causal: bool, bottom_right: bool = False):
+    """Packed variable-length batch (see above): q [Tq,H,D], k/v [Tk,H_kv,D],
+    cu_q/cu_k the B+1 sequence offsets along the token axis. Sequence b is
+    attended on its own; with ``causal`` its diagonal has offset 0 (top-left)
+    or Sk_b - Sq_b (``bottom_right``). Returns O [Tq,H,D], lse [H,Tq]."""
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    if len(cu_q) != len(cu_k) or len(cu_q) < 2:
+        raise ValueError("cu_q and cu_k must hold the same number (B+1 >= 2) of offsets")
+    if cu_q[0] != 0 or cu_k[0] != 0 or cu_q[-1] != q.shape[0] or cu_k[-1] != k.shape[0]:
+        raise ValueError("offsets must run from 0 to the packed lengths")
+    if any(b < a for a, b in zip(cu_q, cu_q[1:])) or any(b < a for a, b in zip(cu_k, cu_k[1:])):
+        raise ValueError("offsets must be nondecreasing")
+    Tq, H, D = q.shape
+    o = np.zeros((Tq, H, D), np.float64)
+    lse = np.full((H, Tq), -np.inf)
+    for b in range(len(cu_q) - 1):
+        qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if qe == qs:
+            continue
+        # one BNSD problem with batch 1: [1, heads, tokens, D]
+        qb = q[qs:qe].transpose(1, 0, 2)[None]
+        kb = k[ks:ke].transpose(1, 0, 2)[None]
+        vb = v[ks:ke].transpose(1, 0, 2)[None]
+        off = (ke - ks) - (qe - qs) if bottom_right else 0
+        ob, lb = attention_fp64(qb, kb, vb, scale, causal, off)
+        o[qs:qe] = ob[0].transpose(1, 0, 2)
+        lse[:, qs:qe] = lb[0]
     return o, lse
 
 

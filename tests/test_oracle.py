@@ -15,7 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_bruteforce, attention_fp64, attention_rows_fp64, head_forward
+from oracle import (attention_bruteforce, attention_fp64, attention_rows_fp64,
+                    attention_varlen_fp64, head_forward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
 
@@ -442,3 +443,185 @@ def test_grouped_shifted_pins_accept_correct_copy():
     fn = _xmutant("none")
     for pin in XPINS:
         pin(fn)
+
+
+# ------------------------------------------------ variable-length pins ----
+# Packed sequences: q [Tq,H,D], k/v [Tk,H_kv,D], offsets cu_q, cu_k; each
+# sequence is attended on its own, its diagonal placed inside it; lse [H,Tq].
+
+# (query lengths, key lengths): a sequence without queries, one without
+# keys, Sq > Sk and Sq < Sk, a single token
+VCASES = [([3, 0, 5, 2, 1], [4, 2, 3, 0, 1]), ([1, 4], [6, 1]), ([5], [5]),
+          ([2, 6, 3], [2, 2, 7])]
+
+
+def _packed(lq, lk, H, Hkv, D, seed):
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int64)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int64)
+    q = rand((int(cu_q[-1]), H, D), seed)
+    k = rand((int(cu_k[-1]), Hkv, D), seed + 1)
+    v = rand((int(cu_k[-1]), Hkv, D), seed + 2)
+    return q, k, v, cu_q, cu_k
+
+
+def vpin_bruteforce(fn):
+    """Token by token against the pure-Python loops: query token t finds its
+    sequence by scanning the offsets, and that sequence's keys are handed to
+    the loops as a batch of one."""
+    for c, (lq, lk) in enumerate(VCASES):
+        for (H, Hkv, causal, br) in ((4, 2, True, True), (2, 1, True, False), (3, 3, False, False)):
+            q, k, v, cu_q, cu_k = _packed(lq, lk, H, Hkv, 2, 170 + c)
+            o, lse = fn(q, k, v, cu_q, cu_k, 0.8, causal, br)
+            assert o.shape == q.shape and lse.shape == (H, q.shape[0])
+            for t in range(q.shape[0]):
+                b = 0
+                while not (cu_q[b] <= t < cu_q[b + 1]):
+                    b += 1
+                i = t - cu_q[b]
+                ks, ke = int(cu_k[b]), int(cu_k[b + 1])
+                off = (ke - ks) - int(cu_q[b + 1] - cu_q[b]) if br else 0
+                qq = [[[q[t, h].tolist()] for h in range(H)]]
+                kk = [[k[ks:ke, g].tolist() for g in range(Hkv)]]
+                vv = [[v[ks:ke, g].tolist() for g in range(Hkv)]]
+                # row i of the sequence, seen as row 0 with the diagonal moved by i
+                ob, lb = attention_bruteforce(qq, kk, vv, 0.8, causal, off + i)
+                for h in range(H):
+                    assert np.max(np.abs(o[t, h] - np.array(ob[0][h][0]))) <= 1e-12
+                    if lb[0][h][0] == -math.inf:
+                        assert lse[h, t] == -np.inf and np.all(o[t, h] == 0.0)
+                    else:
+                        assert abs(lse[h, t] - lb[0][h][0]) <= 1e-12
+
+
+def vpin_block_diagonal_sdpa(fn):
+    """The whole packed batch as one attention call of torch's
+    scaled_dot_product_attention (fp64, CPU) with a block-diagonal boolean
+    mask (and the per-sequence diagonal); rows without a visible key, where
+    the library gives NaN, must be O = 0 and lse = -inf."""
+    for c, (lq, lk) in enumerate(VCASES):
+        for causal, br in ((False, False), (True, False), (True, True)):
+            H, Hkv = 4, 2
+            q, k, v, cu_q, cu_k = _packed(lq, lk, H, Hkv, 8, 180 + c)
+            o, lse = fn(q, k, v, cu_q, cu_k, 0.4, causal, br)
+            Tq, Tk = q.shape[0], k.shape[0]
+            keep = torch.zeros(Tq, Tk, dtype=torch.bool)
+            for b in range(len(lq)):
+                qs, qe, ks, ke = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+                i = torch.arange(qe - qs)[:, None]
+                j = torch.arange(ke - ks)[None, :]
+                off = (ke - ks) - (qe - qs) if br else 0
+                blk = (j <= i + off) if causal else torch.ones(qe - qs, ke - ks, dtype=torch.bool)
+                keep[qs:qe, ks:ke] = blk
+            tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+            tk = torch.from_numpy(np.repeat(k, H // Hkv, axis=1)).permute(1, 0, 2)[None]
+            tv = torch.from_numpy(np.repeat(v, H // Hkv, axis=1)).permute(1, 0, 2)[None]
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                tq, tk, tv, attn_mask=keep, scale=0.4)[0].permute(1, 0, 2).numpy()
+            rows = keep.any(dim=1).numpy()
+            assert o.shape == ref.shape
+            assert np.max(np.abs(o[rows] - ref[rows]), initial=0.0) <= 1e-10
+            assert np.all(o[~rows] == 0.0) and np.all(lse[:, ~rows] == -np.inf)
+            assert np.all(np.isfinite(lse[:, rows]))
+
+
+def vpin_sequence_order(fn):
+    """Reordering the sequences of a batch reorders the results and changes
+    nothing else."""
+    lq, lk = [3, 1, 4, 2], [2, 5, 4, 3]
+    q, k, v, cu_q, cu_k = _packed(lq, lk, 2, 1, 4, 190)
+    o, lse = fn(q, k, v, cu_q, cu_k, 0.5, True, True)
+    order = [2, 0, 3, 1]
+    qi = np.concatenate([np.arange(cu_q[b], cu_q[b + 1]) for b in order])
+    ki = np.concatenate([np.arange(cu_k[b], cu_k[b + 1]) for b in order])
+    cq = np.concatenate([[0], np.cumsum([lq[b] for b in order])])
+    ck = np.concatenate([[0], np.cumsum([lk[b] for b in order])])
+    o2, l2 = fn(q[qi], k[ki], v[ki], cq, ck, 0.5, True, True)
+    l1 = lse[:, qi]
+    fin = np.isfinite(l1)
+    assert np.array_equal(np.isfinite(l2), fin) and np.all(l2[~fin] == l1[~fin])
+    assert np.max(np.abs(o2 - o[qi])) <= 1e-14 and np.max(np.abs(l2[fin] - l1[fin])) <= 1e-14
+
+
+VPINS = [vpin_bruteforce, vpin_block_diagonal_sdpa, vpin_sequence_order]
+
+
+@pytest.mark.parametrize("pin", VPINS, ids=lambda p: p.__name__)
+def test_oracle_varlen_pin(pin):
+    pin(attention_varlen_fp64)
+
+
+def test_oracle_varlen_rejects_bad_offsets():
+    q, k, v, cu_q, cu_k = _packed([2, 3], [3, 2], 2, 1, 4, 195)
+    for bq, bk in ((cu_q[:-1], cu_k), (cu_q + 1, cu_k), (cu_q, cu_k[::-1].copy()),
+                   (np.array([0, 4, 3, 5]), np.array([0, 1, 2, 5]))):
+        with pytest.raises(ValueError):
+            attention_varlen_fp64(q, k, v, bq, bk, 0.5, False)
+
+
+def _vmutant(kind):
+    """Independent scaffold for the variable-length pins, with one planted
+    mistake per kind ("none": correct)."""
+    def fn(q, k, v, cu_q, cu_k, scale, causal, br):
+        Tq, H, D = q.shape
+        Hkv = k.shape[1]
+        o = np.zeros((Tq, H, D))
+        lse = np.full((H, Tq), -np.inf)
+        kcu = cu_q if kind == "keys_by_query_offsets" else cu_k
+        for b in range(len(cu_q) - 1):
+            qs, qe = int(cu_q[b]), int(cu_q[b + 1])
+            ks, ke = int(kcu[b]), int(kcu[b + 1])
+            ks = 0 if kind == "keys_from_start" else ks
+            ke = min(ke, k.shape[0])
+            if kind == "global_offset":
+                off = (k.shape[0] - Tq) if br else 0
+            else:
+                off = (ke - ks) - (qe - qs) if br else 0
+            for h in range(H):
+                g = h // (H // Hkv)
+                for i in range(qe - qs):
+                    s = k[ks:ke, g] @ q[qs + i, h] * scale
+                    if causal:
+                        s = np.where(np.arange(ke - ks) > i + off, -np.inf, s)
+                    if (s.size == 0 or np.all(np.isneginf(s))) and kind != "empty_rows_nan":
+                        continue
+                    with np.errstate(all="ignore"):
+                        m = s.max() if s.size else -np.inf
+                        p = np.exp(s - m)
+                        o[qs + i, h] = p @ v[ks:ke, g] / p.sum()
+                        lse[h, qs + i] = m + np.log(p.sum())
+        if kind == "lse_token_major":
+            return o, lse.T.copy()
+        return o, lse
+    return fn
+
+
+VMUTANTS = ["keys_by_query_offsets", "keys_from_start", "global_offset", "empty_rows_nan",
+            "lse_token_major"]
+
+
+@pytest.mark.parametrize("kind", VMUTANTS)
+def test_varlen_pins_catch_planted_mistakes(kind):
+    fn = _vmutant(kind)
+    failed = []
+    for pin in VPINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(fn)
+        except (AssertionError, ValueError, IndexError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {kind!r}"
+
+
+def test_varlen_pins_accept_correct_copy():
+    fn = _vmutant("none")
+    for pin in VPINS:
+        pin(fn)
+
+
+def test_oracle_empty_key_set():
+    """No key at all: every row is without a visible key."""
+    q = rand((1, 2, 3, 4), 197)
+    z = np.zeros((1, 1, 0, 4))
+    for causal, off in ((False, 0), (True, 0), (True, 5)):
+        o, lse = attention_fp64(q, z, z, 0.5, causal, off)
+        assert np.all(o == 0.0) and np.all(lse == -np.inf)
