@@ -35,7 +35,7 @@ FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL_TOP_LEFT, FA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-           "fa_status_str", "fa_abi_version")
+           "fa_fwd_varlen", "fa_status_str", "fa_abi_version")
 
 _lib = None
 
@@ -69,6 +69,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                               ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
                               ctypes.c_int, ctypes.c_int, vp, vp, vp,
                               ctypes.c_int, vp, i64, vp]
+    lib.fa_fwd_varlen.restype = ctypes.c_int
+    lib.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp,         # q k v o lse cu_q cu_k
+                                  i64, i64, i64, i64, i64, i64, i64,  # B H H_kv tq tk maxq D
+                                  ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                                  ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
     lib.fa_fwd_splitkv_workspace_size.restype = i64
     lib.fa_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -109,6 +114,16 @@ def fa_fwd_ex_raw(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask, k
     return load_library().fa_fwd_ex(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask,
                                     keep_prob, in_dtype, o_dtype, descale_q, descale_k,
                                     descale_v, num_splits, workspace, workspace_size, stream)
+
+
+def fa_fwd_varlen_raw(q, k, v, o, lse, cu_q, cu_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
+                      D, scale, mask, keep_prob, in_dtype, o_dtype, descale_q, descale_k,
+                      descale_v, stream) -> int:
+    """The packed variable-length C entry point with integer pointers."""
+    return load_library().fa_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, H_kv, total_q,
+                                        total_k, max_seqlen_q, D, scale, mask, keep_prob,
+                                        in_dtype, o_dtype, descale_q, descale_k, descale_v,
+                                        stream)
 
 
 def splitkv_workspace_size(B, H, Sq, Sk, D, causal=False, num_splits=0) -> int:
@@ -174,6 +189,61 @@ def fa_fwd_splitkv(q, k, v, *, num_splits: int = 0, scale: float | None = None,
     bytes (allocated here when not given)."""
     return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
                  out, lse, stream, int(num_splits), workspace, layout)
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
+                  scale: float | None = None, causal: bool = False, keep_prob: float = 1.0,
+                  o_dtype=None, descale_q=None, descale_k=None, descale_v=None, out=None,
+                  lse=None, stream=None):
+    """Attention forward over a batch of sequences of different lengths.
+
+    q [total_q,H,D], k/v [total_k,H_kv,D]: the sequences packed one after
+    the other (contiguous GPU tensors); ``cu_seqlens_q``/``cu_seqlens_k``:
+    int32 GPU tensors of B+1 offsets from 0 to total_q (total_k), sequence b
+    owning rows cu[b]..cu[b+1]-1; ``max_seqlen_q``: the longest query
+    length. Each sequence is attended on its own (``causal`` as in fa_fwd,
+    per sequence). Returns (o [total_q,H,D], lse [H,total_q] fp32).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [total, heads, D]")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must be 1-D of the same length B+1")
+    tq, H, D = q.shape
+    tk, Hkv = k.shape[0], k.shape[1]
+    if tuple(k.shape) != (tk, Hkv, D) or tuple(v.shape) != (tk, Hkv, D):
+        raise ValueError("k and v must be [total_k, H_kv, D] with q's D")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise ValueError("q, k, v must share a dtype")
+    B = cu_seqlens_q.shape[0] - 1
+    if o_dtype is None:
+        o_dtype = torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float16
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if out is None:
+        out = torch.empty(tuple(q.shape), dtype=o_dtype, device=dev)
+    if lse is None:
+        lse = torch.empty((H, tq), dtype=torch.float32, device=dev)
+    dq = descale_q.data_ptr() if descale_q is not None else None
+    dk = descale_k.data_ptr() if descale_k is not None else None
+    dv = descale_v.data_ptr() if descale_v is not None else None
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check_status(fa_fwd_varlen_raw(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, H, Hkv, tq, tk, int(max_seqlen_q),
+        D, float(scale), _mask_code(causal), float(keep_prob), _dtype_code(q.dtype),
+        _dtype_code(out.dtype), dq, dk, dv, stream))
+    return out, lse
 
 
 def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,

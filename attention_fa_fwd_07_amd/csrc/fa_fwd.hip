@@ -79,6 +79,14 @@ struct Params {
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int64_t moff;         // causal: key j is visible to query i iff j <= i + moff
+  // variable lengths: cumulative query and key lengths of the B sequences
+  // ([B+1] each, device); nullptr for fixed lengths Sq, Sk. Rows of sequence
+  // b start at row cu[b] of the packed tensors; Sq, Sk are then the packed
+  // totals, lse is [H, total_q], and a bottom-right diagonal (br) is placed
+  // per sequence.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t br;
   float scale_log2;     // |scale| * log2(e)
   int32_t negate;       // scale < 0: Q fragments are negated (exact)
   // split-KV only: key-tile ranges per query block, partial results
@@ -300,6 +308,9 @@ struct FwdTile {
   const char* vhead;
   int kpitch;                       // bytes from one K/V row to the next in HBM
   int64_t qbase;                    // element offset of this (batch, head) in q and o
+  int64_t lse_base;                 // index of this block's row 0 in lse
+  int64_t moff;                     // causal: key j is visible to query i iff j <= i + moff
+  bool idle;                        // variable lengths: no row of this block exists
   float c;                          // softmax scale in log2 units (fp8: times dq * dk)
 
   qfrag_t qf[NDS];
@@ -328,16 +339,37 @@ struct FwdTile {
     Sq = p.Sq;
     Sk = p.Sk;
     q0 = (int64_t)qb * BM;
+    moff = p.moff;
+    idle = false;
     {
       const int b = bh / p.H;
       const int h = bh - b * p.H;
       const int kvh = h / (p.H / p.Hkv);
-      const int64_t koff = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+      int64_t koff = (int64_t)b * p.k_sb + (int64_t)kvh * p.k_sh;
+      qbase = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
+      lse_base = (int64_t)bh * Sq;
+      if (p.cu_q) {
+        // sequence b: its start and length, clamped into the packed tensors
+        // (malformed arrays give undefined results, never a stray access)
+        int64_t qs = p.cu_q[b], qe = p.cu_q[b + 1];
+        int64_t ks = p.cu_k[b], ke = p.cu_k[b + 1];
+        qs = qs < 0 ? 0 : (qs > Sq ? Sq : qs);
+        qe = qe < qs ? qs : (qe > Sq ? Sq : qe);
+        ks = ks < 0 ? 0 : (ks > Sk ? Sk : ks);
+        ke = ke < ks ? ks : (ke > Sk ? Sk : ke);
+        lse_base = (int64_t)h * Sq + qs;      // lse [H, total_q]
+        qbase = qs * p.q_ss + (int64_t)h * p.q_sh;
+        koff = ks * p.k_ss + (int64_t)kvh * p.k_sh;
+        Sq = qe - qs;
+        Sk = ke - ks;
+        if (p.br) moff = Sk - Sq;
+        idle = q0 >= Sq;                      // past this sequence's last row
+      }
       khead = p.k + koff * ES;
       vhead = p.v + koff * ES;
       kpitch = (int)(p.k_ss * ES);
-      qbase = (int64_t)b * p.q_sb + (int64_t)h * p.q_sh;
     }
+    if (idle) return;
     qw0 = q0 + wave * 32;
     qrow = qw0 + l32;
     c = p.scale_log2;
@@ -345,7 +377,7 @@ struct FwdTile {
 
     int64_t kend = Sk;
     if constexpr (CAUSAL) {
-      kend = (q0 + BM + p.moff) < Sk ? (q0 + BM + p.moff) : Sk;
+      kend = (q0 + BM + moff) < Sk ? (q0 + BM + moff) : Sk;
       if (kend < 0) kend = 0;   // every row of the block lies above the diagonal
     }
     ntiles = (int)((kend + BN - 1) / BN);
@@ -360,7 +392,7 @@ struct FwdTile {
     }
     jlast = ntiles - 1;   // last tile this wave needs
     if constexpr (CAUSAL) {
-      const int64_t last_key = qw0 + 31 + p.moff;   // last key any row of this wave sees
+      const int64_t last_key = qw0 + 31 + moff;   // last key any row of this wave sees
       const int64_t jl = last_key < 0 ? -1 : last_key / BN;
       jlast = jl < jlast ? (int)jl : jlast;
     }
@@ -561,7 +593,7 @@ struct FwdTile {
     // mask: keys past Sk, keys above the diagonal. key = kt0 + kb*32 +
     // 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or > this row's query:
     // compare the compile-time part with a per-lane limit.
-    const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > qw0 + p.moff);
+    const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > qw0 + moff);
     if (need_mask) {
       // keeps this a branch: full tiles (all but the last, or the diagonal
       // ones) then skip the compare-and-select on every score
@@ -569,7 +601,7 @@ struct FwdTile {
       const int64_t kv = Sk - kt0;
       int lim = kv < BN ? (int)kv : BN;
       if constexpr (CAUSAL) {
-        int64_t qr = qrow + p.moff - kt0 + 1;
+        int64_t qr = qrow + moff - kt0 + 1;
         if (qr < 0) qr = 0;
         lim = qr < lim ? (int)qr : lim;
       }
@@ -706,6 +738,7 @@ struct FwdTile {
   }
 
   __device__ __forceinline__ void run() {
+    if (idle) return;   // uniform over the workgroup: no barrier is left waiting
     // tile j lives in buffer (j - jbeg) % NB; tiles j+1 .. j+NB-1 are in flight
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
@@ -747,7 +780,7 @@ struct FwdTile {
       }
     }
     if (hl == 0) {
-      p.lse[(int64_t)bh * Sq + qrow] = any ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
+      p.lse[lse_base + qrow] = any ? (m_run + __builtin_amdgcn_logf(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
   }
 
@@ -976,6 +1009,9 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
   // one K/V row pitch in bytes must fit the 32-bit per-lane load offsets
   if (p.k_ss * ie * 32 > INT32_MAX) return FA_ERR_BAD_SHAPE;
   p.moff = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT ? Sk - Sq : 0;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
+  p.br = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT;
   c.nw = nw;
   c.BH = BH;
   c.nqb = nqb;
@@ -1141,6 +1177,35 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   return fa_fwd_ex(q, k, v, o, lse, B, H, H, Sq, Sk, D, layout, scale,
                    causal ? FA_MASK_CAUSAL_TOP_LEFT : FA_MASK_NONE, keep_prob, in_dtype, o_dtype,
                    descale_q, descale_k, descale_v, num_splits, workspace, workspace_size, stream);
+}
+
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t total_q, int64_t total_k,
+                          int64_t max_seqlen_q, int64_t D, float scale, fa_mask_t mask,
+                          float keep_prob, fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                          const float* descale_q, const float* descale_k, const float* descale_v,
+                          hipStream_t stream) {
+  // the packed tensors are checked as one sequence-major batch of total_q
+  // query and total_k key rows
+  Call c;
+  const fa_status_t st = check_call(q, k, v, o, lse, 1, H, H_kv, total_q, total_k, D, FA_LAYOUT_BSHD,
+                                    scale, mask, keep_prob, in_dtype, o_dtype, descale_q, descale_k,
+                                    descale_v, c);
+  if (st != FA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k) return FA_ERR_NULL_POINTER;
+  if (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3) return FA_ERR_MISALIGNED;
+  if (B < 1 || B > INT32_MAX / 2 || max_seqlen_q < 1 || max_seqlen_q > total_q) return FA_ERR_BAD_SHAPE;
+  const int64_t nqb = (max_seqlen_q + 32 * c.nw - 1) / (32 * c.nw);
+  if (B * H * nqb > INT32_MAX) return FA_ERR_BAD_SHAPE;
+  Params p = c.p;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.moff = 0;
+  p.nqb = (int32_t)nqb;
+  p.total = (int32_t)(B * H * nqb);
+  hipLaunchKernelGGL(pick_kernel<false>(c), dim3((unsigned)p.total), dim3(64 * c.nw), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
 }  // extern "C"

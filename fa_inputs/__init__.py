@@ -156,3 +156,37 @@ def values(inp: Inputs) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
     """float64 q, k, v values as the kernel sees them."""
     return (as_float64(inp.q, inp.descale_q), as_float64(inp.k, inp.descale_k),
             as_float64(inp.v, inp.descale_v))
+
+
+@dataclass
+class VarlenInputs:
+    """A packed batch of sequences of different lengths (CPU tensors):
+    q [Tq,H,D], k/v [Tk,H_kv,D]; ``cu_q``/``cu_k`` int32 [B+1] offsets."""
+
+    inp: Inputs
+    cu_q: torch.Tensor
+    cu_k: torch.Tensor
+    max_q: int
+
+
+def make_varlen_inputs(lens_q, lens_k, H: int, Hkv: int, D: int, dtype: str, seed: int,
+                       amp: float = 1.0) -> VarlenInputs:
+    """Seeded packed inputs: standard normal float64 draws of shapes
+    (Tq,H,D), (Tk,Hkv,D), (Tk,Hkv,D) in the order q, k, v (times ``amp``),
+    cast or quantised per tensor as ``make_inputs`` does."""
+    if len(lens_q) != len(lens_k) or not lens_q:
+        raise ValueError("one query and one key length per sequence")
+    tq, tk = int(sum(lens_q)), int(sum(lens_k))
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((tq, H, D)) * amp
+    k = rng.standard_normal((tk, Hkv, D)) * amp
+    v = rng.standard_normal((tk, Hkv, D)) * amp
+    if dtype == FP8:
+        (cq, sq), (ck, sk), (cv, sv) = quantize_e4m3(q), quantize_e4m3(k), quantize_e4m3(v)
+        inp = Inputs(cq, ck, cv, sq, sk, sv)
+    else:
+        td = TORCH_DTYPE[dtype]
+        inp = Inputs(*(torch.from_numpy(x).to(torch.float32).to(td) for x in (q, k, v)))
+    cu_q = torch.tensor([0] + list(np.cumsum(lens_q)), dtype=torch.int32)
+    cu_k = torch.tensor([0] + list(np.cumsum(lens_k)), dtype=torch.int32)
+    return VarlenInputs(inp, cu_q, cu_k, int(max(lens_q)))

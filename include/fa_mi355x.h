@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 3
+#define FA_ABI_VERSION 4
 
 typedef enum {
   FA_OK = 0,
@@ -180,6 +180,30 @@ fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, floa
                       const float* descale_q, const float* descale_k, const float* descale_v,
                       int num_splits, void* workspace, int64_t workspace_size,
                       hipStream_t stream);
+
+/*
+ * fa_fwd_varlen — B sequences of different lengths in packed, sequence-major
+ * tensors: q and o [total_q, H, D], k and v [total_k, H_kv, D] (element
+ * (t, h, d) at (t*H + h)*D + d), sequence b owning query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1. cu_seqlens_q, cu_seqlens_k: device int32 arrays of
+ * B+1 nondecreasing offsets from 0 to total_q (total_k). max_seqlen_q: the
+ * longest query length (sizes the grid; rows beyond it are not computed).
+ * lse: fp32 [H, total_q]. Each sequence is attended on its own, with the
+ * mask (and the bottom-right diagonal) placed per sequence; a sequence
+ * with no key gives O = 0 and lse = -inf. The library does not read the
+ * offsets on the host: offsets that break the rules above give undefined
+ * results (the kernel clamps them into the packed tensors, so it never
+ * reads or writes outside them). Other arguments and errors as fa_fwd_ex;
+ * no split-KV. One kernel on `stream`.
+ */
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int64_t B, int64_t H, int64_t H_kv, int64_t total_q, int64_t total_k,
+                          int64_t max_seqlen_q, int64_t D, float scale, fa_mask_t mask,
+                          float keep_prob, fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                          const float* descale_q, const float* descale_k, const float* descale_v,
+                          hipStream_t stream);
 
 /* Human-readable name of a status code ("FA_OK", ...); never NULL. */
 const char* fa_status_str(fa_status_t s);

@@ -41,7 +41,7 @@ def test_library_holds_gfx950_code():
 
 def test_abi_version_and_status_strings():
     lib = fa.load_library()
-    assert lib.fa_abi_version() == 3
+    assert lib.fa_abi_version() == 4
     names = [fa.status_str(c) for c in range(13)]
     assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP" and names[11] == "FA_ERR_WORKSPACE"
     assert names[12] == "FA_ERR_UNSUPPORTED_MASK"
@@ -183,3 +183,48 @@ def test_python_wrapper_rejects_unknown_mask():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa._mask_code("diagonal")
+
+
+# ---- the variable-length entry point ----
+CQ, CK = 0x7100000, 0x7200000   # fake offset arrays
+
+
+def call_varlen(**over):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, cu_q=CQ, cu_k=CK, B=3, H=4, H_kv=2, total_q=300,
+             total_k=400, max_seqlen_q=200, D=128, scale=0.125, mask=fa.FA_MASK_NONE,
+             keep_prob=1.0, in_dtype=fa.FA_F16, o_dtype=fa.FA_F16, descale_q=None,
+             descale_k=None, descale_v=None, stream=None)
+    a.update(over)
+    return fa.fa_fwd_varlen_raw(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(cu_q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(cu_k=None), fa.FA_ERR_NULL_POINTER),
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(cu_q=CQ + 2), fa.FA_ERR_MISALIGNED),
+    (dict(cu_k=CK + 1), fa.FA_ERR_MISALIGNED),
+    (dict(B=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(max_seqlen_q=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(max_seqlen_q=301), fa.FA_ERR_BAD_SHAPE),
+    (dict(total_q=0, max_seqlen_q=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(total_k=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(H_kv=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(mask=7), fa.FA_ERR_UNSUPPORTED_MASK),
+    (dict(keep_prob=0.5), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    # o [total_q, H, D] overlapping k [total_k, H_kv, D]
+    (dict(o=K + 256), fa.FA_ERR_ALIASING),
+    # lse [H, total_q] fp32 right after o is fine, inside it is not
+    (dict(lse=O + 1024), fa.FA_ERR_ALIASING),
+])
+def test_varlen_rejects_before_launch(over, code):
+    assert call_varlen(**over) == code
+
+
+def test_varlen_wrapper_checks_offsets():
+    import torch
+    x = torch.zeros(8, 2, 64, dtype=torch.float16)
+    cu = torch.tensor([0, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        fa.fa_fwd_varlen(x, x, x, cu, cu, 8)          # CPU tensors
