@@ -87,6 +87,7 @@ struct Params {
   const int32_t* cu_q;
   const int32_t* cu_k;
   int32_t br;
+  int32_t xcd_unit;     // > 0: launch-order groups dealt round-robin to the XCDs
   float scale_log2;     // |scale| * log2(e)
   int32_t negate;       // scale < 0: Q fragments are negated (exact)
   // split-KV only: key-tile ranges per query block, partial results
@@ -228,6 +229,16 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
   const int base = n >> 3, rem = n & 7;
   return xcd * base + (xcd < rem ? xcd : rem) + local;
 }
+// The same with the launch order cut into groups of `unit` adjacent blocks
+// (the blocks of one head, or of the heads sharing one key/value head) dealt
+// round-robin to the XCDs: XCD x runs groups x, x+8, ... (needs n/unit to be
+// a multiple of 8). Used when the groups differ in work (variable lengths):
+// every XCD then gets a share of every sequence.
+__device__ __forceinline__ int xcd_deal(int w, int unit) {
+  const int xcd = w & 7, local = w >> 3;
+  const int g = local / unit;
+  return (xcd + 8 * g) * unit + (local - g * unit);
+}
 
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
 // (lgkmcnt) but not for its HBM->LDS loads, which are waited for explicitly
@@ -327,7 +338,7 @@ struct FwdTile {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hl = lane >> 5;
     l32 = lane & 31;
-    int t = xcd_remap(blockIdx.x, p.total);
+    int t = p.xcd_unit ? xcd_deal(blockIdx.x, p.xcd_unit) : xcd_remap(blockIdx.x, p.total);
     split = 0;
     if constexpr (SPLIT) {
       split = t % p.nsplit;          // the ranges of a block are adjacent, on one XCD
@@ -1012,6 +1023,7 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
   p.cu_q = nullptr;
   p.cu_k = nullptr;
   p.br = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT;
+  p.xcd_unit = 0;
   c.nw = nw;
   c.BH = BH;
   c.nqb = nqb;
@@ -1204,6 +1216,13 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   p.moff = 0;
   p.nqb = (int32_t)nqb;
   p.total = (int32_t)(B * H * nqb);
+  // sequences differ in work: deal each key/value head's blocks (else each
+  // head's) round-robin to the 8 XCDs so they stay balanced and the blocks
+  // sharing K/V still share one XCD's L2
+  if ((B * H_kv) % 8 == 0)
+    p.xcd_unit = (int32_t)((H / H_kv) * nqb);
+  else if ((B * H) % 8 == 0)
+    p.xcd_unit = (int32_t)nqb;
   hipLaunchKernelGGL(pick_kernel<false>(c), dim3((unsigned)p.total), dim3(64 * c.nw), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -128,3 +128,20 @@ def test_varlen_equal_lengths_match_fixed_path_bitwise(causal):
     # lse: [H, B*S] against [B, H, S]
     assert torch.equal(l1.view(H, B, S).permute(1, 0, 2).contiguous().view(torch.int32),
                        l2.view(torch.int32))
+
+
+@pytest.mark.parametrize("H,Hkv,nseq", [(8, 2, 4), (8, 2, 9), (3, 1, 5)])
+def test_varlen_launch_orders(H, Hkv, nseq):
+    """The three launch orders: key/value-head groups dealt to the XCDs
+    (B*H_kv a multiple of 8), heads dealt (only B*H a multiple of 8), and
+    the contiguous order (neither)."""
+    rng = np.random.default_rng(1280 + nseq)
+    lq = [int(x) for x in rng.integers(1, 400, nseq)]
+    lk = [int(x) for x in rng.integers(0, 400, nseq)]
+    vi = fi.make_varlen_inputs(lq, lk, H, Hkv, 64, fi.BF16, seed=1281 + nseq)
+    q64, k64, v64 = fi.values(vi.inp)
+    for mask in MASKS:
+        ref_o, ref_l = attention_varlen_fp64(q64, k64, v64, vi.cu_q.numpy(), vi.cu_k.numpy(),
+                                             0.125, mask != "none", mask == "bottom_right")
+        o, lse = run_varlen(vi, 0.125, MASKS[mask], fi.F32)
+        check(fi.BF16, fi.F32, o, lse, ref_o, ref_l, f"H{H}/{Hkv} B{nseq} {mask}")
