@@ -38,6 +38,17 @@ that FlashAttention reaches exactly, up to rounding order:
     scaled, masked score row. The pages never define lse; this is the
     reading adopted for the per-row logsumexp output.
 
+The backward (``attention_bwd_fp64``) is the gradient of that same
+function: for a cotangent dO of O, with P the row-softmax above,
+  dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(P * dP)),
+  dQ = scale * dS K,  dK = scale * dS^T Q
+(the chain rule through O = P V, the softmax Jacobian diag(p) - p p^T and
+S = scale * Q K^T; masked entries have P = 0 and pass no gradient). With
+grouped heads, dK and dV of a key/value head sum over its query heads. The
+pages mention the backward's dQ pass only for a stride defect ("Hygon
+FlashAttention: fixed-defect review", item 13) and state none of its
+formulas; these are the derivative of the forward definition.
+
 Everything is float64 from the exact input values. S and P are
 materialised per (batch, head).
 
@@ -147,6 +158,31 @@ def attention_varlen_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_
         o[qs:qe] = ob[0].transpose(1, 0, 2)
         lse[:, qs:qe] = lb[0]
     return o, lse
+
+
+def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                       scale: float, causal: bool, offset: int = 0):
+    """Gradients of the BNSD forward for the cotangent ``do`` [B,H,Sq,D]:
+    returns dq [B,H,Sq,D], dk, dv [B,H_kv,Sk,D]."""
+    group = _check(q, k, v)
+    if do.shape != q.shape:
+        raise ValueError("do must have q's shape")
+    B, H, Sq, D = q.shape
+    dq = np.zeros(q.shape)
+    dk = np.zeros(k.shape)
+    dv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            kv = h // group
+            _, _, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal,
+                                   return_p=True, offset=offset)
+            g = np.asarray(do[b, h], np.float64)
+            dv[b, kv] += p.T @ g                                       # dV = P^T dO
+            dp = g @ np.asarray(v[b, kv], np.float64).T                # dP = dO V^T
+            ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))      # softmax Jacobian
+            dq[b, h] = scale * (ds @ np.asarray(k[b, kv], np.float64))  # dQ = scale dS K
+            dk[b, kv] += scale * (ds.T @ np.asarray(q[b, h], np.float64))   # dK = scale dS^T Q
+    return dq, dk, dv
 
 
 def attention_rows_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,

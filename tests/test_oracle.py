@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention_bruteforce, attention_fp64, attention_rows_fp64,
-                    attention_varlen_fp64, head_forward)
+from oracle import (attention_bruteforce, attention_bwd_fp64, attention_fp64,
+                    attention_rows_fp64, attention_varlen_fp64, head_forward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
 
@@ -625,3 +625,147 @@ def test_oracle_empty_key_set():
     for causal, off in ((False, 0), (True, 0), (True, 5)):
         o, lse = attention_fp64(q, z, z, 0.5, causal, off)
         assert np.all(o == 0.0) and np.all(lse == -np.inf)
+
+
+# ------------------------------------------------------- backward pins ----
+# fn(q, k, v, do, scale, causal, offset) -> (dq, dk, dv): the gradient of
+# L = sum(O * dO) with respect to q, k, v.
+
+def _loss_bruteforce(q, k, v, do, scale, causal, offset):
+    o, _ = attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), scale, causal, offset)
+    return math.fsum(a * b for a, b in zip(np.asarray(o).ravel().tolist(), do.ravel().tolist()))
+
+
+def bpin_finite_differences(fn):
+    """Central differences of the pure-Python forward (loss sum(O * dO)),
+    every element of q, k and v, grouped heads and shifted diagonals (one
+    case with rows that see no key)."""
+    h = 1e-5
+    for (B, H, Hkv, Sq, Sk, D, causal, off, seed) in [
+        (1, 2, 1, 3, 4, 2, True, 1, 61), (1, 2, 2, 4, 3, 3, False, 0, 62),
+        (1, 4, 2, 4, 2, 2, True, -2, 63), (2, 1, 1, 2, 5, 2, True, 3, 64),
+    ]:
+        q = rand((B, H, Sq, D), seed)
+        k = rand((B, Hkv, Sk, D), seed + 1)
+        v = rand((B, Hkv, Sk, D), seed + 2)
+        do = rand((B, H, Sq, D), seed + 3)
+        dq, dk, dv = fn(q, k, v, do, 0.7, causal, off)
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            assert g.shape == x.shape
+            for idx in np.ndindex(x.shape):
+                keep = x[idx]
+                x[idx] = keep + h
+                lp = _loss_bruteforce(q, k, v, do, 0.7, causal, off)
+                x[idx] = keep - h
+                lm = _loss_bruteforce(q, k, v, do, 0.7, causal, off)
+                x[idx] = keep
+                assert abs((lp - lm) / (2 * h) - g[idx]) <= 1e-7, (idx, g[idx], (lp - lm) / (2 * h))
+
+
+def bpin_torch_autograd(fn):
+    """torch autograd (fp64, CPU) through scaled_dot_product_attention with an
+    explicit boolean mask; grouped heads by repeating K and V (autograd sums
+    the repeats)."""
+    for (H, Hkv, Sq, Sk, causal, off, seed) in [(4, 2, 9, 13, True, 4, 71), (4, 1, 13, 9, True, 0, 72),
+                                                (3, 3, 10, 10, False, 0, 73), (2, 1, 7, 20, True, 13, 74)]:
+        q = rand((1, H, Sq, 8), seed)
+        k = rand((1, Hkv, Sk, 8), seed + 1)
+        v = rand((1, Hkv, Sk, 8), seed + 2)
+        do = rand((1, H, Sq, 8), seed + 3)
+        dq, dk, dv = fn(q, k, v, do, 0.3, causal, off)
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+        keep = (torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + off) if causal else None
+        rk = tk.repeat_interleave(H // Hkv, dim=1)
+        rv = tv.repeat_interleave(H // Hkv, dim=1)
+        out = torch.nn.functional.scaled_dot_product_attention(tq, rk, rv, attn_mask=keep, scale=0.3)
+        out.backward(torch.from_numpy(do))
+        for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.max(np.abs(mine - ref.numpy())) <= 1e-10
+
+
+def bpin_invariants(fn):
+    """Softmax rows sum to 1: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0;
+    constant V rows: O does not depend on q or k (dQ = dK = 0); dO = 0: all
+    gradients 0; rows without a visible key: dQ row = 0."""
+    q = rand((1, 2, 6, 4), 81)
+    k = rand((1, 2, 9, 4), 82)
+    v = rand((1, 2, 9, 4), 83)
+    do = rand((1, 2, 6, 4), 84)
+    for causal, off in ((False, 0), (True, 0), (True, 3)):
+        dq, dk, dv = fn(q, k, v, do, 0.5, causal, off)
+        assert np.max(np.abs(dv.sum(axis=2) - do.sum(axis=2))) <= 1e-12
+        assert np.max(np.abs(dk.sum(axis=2))) <= 1e-12
+    vc = np.broadcast_to(rand((1, 2, 1, 4), 85), v.shape).copy()
+    dq, dk, dv = fn(q, k, vc, do, 0.5, True, 1)
+    assert np.max(np.abs(dq)) <= 1e-12 and np.max(np.abs(dk)) <= 1e-12
+    dq, dk, dv = fn(q, k, v, np.zeros_like(do), 0.5, True, 0)
+    assert not dq.any() and not dk.any() and not dv.any()
+    dq, dk, dv = fn(q, k, v, do, 0.5, True, -2)     # rows 0, 1 see no key
+    assert np.all(dq[:, :, :2] == 0.0) and np.all(np.isfinite(dq))
+
+
+BPINS = [bpin_finite_differences, bpin_torch_autograd, bpin_invariants]
+
+
+@pytest.mark.parametrize("pin", BPINS, ids=lambda p: p.__name__)
+def test_oracle_backward_pin(pin):
+    pin(attention_bwd_fp64)
+
+
+def _bmutant(kind):
+    """Independent scaffold for the backward pins, with one planted mistake
+    per kind ("none": correct)."""
+    def fn(q, k, v, do, scale, causal, offset):
+        B, H, Sq, D = q.shape
+        Hkv, Sk = k.shape[1], k.shape[2]
+        dq = np.zeros(q.shape)
+        dk = np.zeros(k.shape)
+        dv = np.zeros(v.shape)
+        for b in range(B):
+            for h in range(H):
+                g = h // (H // Hkv)
+                s = q[b, h] @ k[b, g].T * scale
+                if causal and kind != "mask_dropped":
+                    s = np.where(np.arange(Sk)[None, :] > np.arange(Sq)[:, None] + offset, -np.inf, s)
+                p = np.zeros_like(s)
+                for r in range(Sq):
+                    if np.all(np.isneginf(s[r])):
+                        continue
+                    e = np.exp(s[r] - s[r].max())
+                    p[r] = e if kind == "unnormalised_p" else e / e.sum()
+                dp = do[b, h] @ v[b, g].T
+                delta = 0.0 if kind == "no_delta" else np.sum(p * dp, axis=1, keepdims=True)
+                ds = p * (dp - delta)
+                dq[b, h] = (1.0 if kind == "dq_unscaled" else scale) * ds @ k[b, g]
+                sign = -1.0 if kind == "dk_sign" else 1.0
+                if kind == "group_overwrites":
+                    dk[b, g] = sign * scale * ds.T @ q[b, h]
+                    dv[b, g] = p.T @ do[b, h]
+                else:
+                    dk[b, g] += sign * scale * ds.T @ q[b, h]
+                    dv[b, g] += p.T @ do[b, h]
+        return dq, dk, dv
+    return fn
+
+
+BMUTANTS = ["mask_dropped", "unnormalised_p", "no_delta", "dq_unscaled", "dk_sign",
+            "group_overwrites"]
+
+
+@pytest.mark.parametrize("kind", BMUTANTS)
+def test_backward_pins_catch_planted_mistakes(kind):
+    fn = _bmutant(kind)
+    failed = []
+    for pin in BPINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(fn)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {kind!r}"
+
+
+def test_backward_pins_accept_correct_copy():
+    fn = _bmutant("none")
+    for pin in BPINS:
+        pin(fn)
