@@ -35,7 +35,8 @@ FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL_TOP_LEFT, FA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-           "fa_fwd_varlen", "fa_status_str", "fa_abi_version")
+           "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
+           "fa_abi_version")
 
 _lib = None
 
@@ -74,6 +75,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   i64, i64, i64, i64, i64, i64, i64,  # B H H_kv tq tk maxq D
                                   ctypes.c_float, ctypes.c_int, ctypes.c_float,
                                   ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    lib.fa_bwd.restype = ctypes.c_int
+    lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp,          # q k v o dout lse
+                           vp, vp, vp,                      # dq dk dv
+                           i64, i64, i64, i64, i64, i64,    # B H H_kv Sq Sk D
+                           ctypes.c_float, ctypes.c_int,    # scale mask
+                           ctypes.c_int, ctypes.c_int,      # in_dtype grad_dtype
+                           vp, i64, vp]                     # workspace size stream
+    lib.fa_bwd_workspace_size.restype = i64
+    lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64]
     lib.fa_fwd_splitkv_workspace_size.restype = i64
     lib.fa_fwd_splitkv_workspace_size.argtypes = [i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int]
     lib.fa_status_str.restype = ctypes.c_char_p
@@ -124,6 +134,19 @@ def fa_fwd_varlen_raw(q, k, v, o, lse, cu_q, cu_k, B, H, H_kv, total_q, total_k,
                                         total_k, max_seqlen_q, D, scale, mask, keep_prob,
                                         in_dtype, o_dtype, descale_q, descale_k, descale_v,
                                         stream)
+
+
+def fa_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D, scale, mask,
+               in_dtype, grad_dtype, workspace, workspace_size, stream) -> int:
+    """The backward C entry point with integer pointers; returns the status code."""
+    return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D,
+                                 scale, mask, in_dtype, grad_dtype, workspace, workspace_size,
+                                 stream)
+
+
+def bwd_workspace_size(B, H, Sq) -> int:
+    """Workspace bytes fa_bwd needs (-1: rejected sizes)."""
+    return load_library().fa_bwd_workspace_size(B, H, Sq)
 
 
 def splitkv_workspace_size(B, H, Sq, Sk, D, causal=False, num_splits=0) -> int:
@@ -244,6 +267,63 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
         D, float(scale), _mask_code(causal), float(keep_prob), _dtype_code(q.dtype),
         _dtype_code(out.dtype), dq, dk, dv, stream))
     return out, lse
+
+
+def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = False,
+           grad_dtype=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Gradients (dq, dk, dv) of the attention forward for the cotangent
+    ``dout``, from the forward's output ``o`` and ``lse``.
+
+    q, o, dout [B,H,Sq,D] and k, v [B,H_kv,Sk,D]: contiguous BNSD GPU tensors
+    of one dtype (fp16 or bf16); lse [B,H,Sq] fp32. ``causal`` as in fa_fwd.
+    ``grad_dtype``: dtype of the gradients (default: the input dtype; or
+    float32). ``workspace``: an optional uint8 GPU tensor of at least
+    ``bwd_workspace_size(B, H, Sq)`` bytes (allocated here when not given).
+    """
+    import torch
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous (BNSD)")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    B, H, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, Sk, D) or tuple(v.shape) != (B, Hkv, Sk, D):
+        raise ValueError("k and v must be [B, H_kv, Sk, D] with q's B and D")
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    if tuple(lse.shape) != (B, H, Sq) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [B, H, Sq]")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
+        raise ValueError("q, k, v, o, dout must share a dtype")
+    if grad_dtype is None:
+        grad_dtype = q.dtype
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dev = q.device
+    if dq is None:
+        dq = torch.empty(tuple(q.shape), dtype=grad_dtype, device=dev)
+    if dk is None:
+        dk = torch.empty(tuple(k.shape), dtype=grad_dtype, device=dev)
+    if dv is None:
+        dv = torch.empty(tuple(v.shape), dtype=grad_dtype, device=dev)
+    need = bwd_workspace_size(B, H, Sq)
+    if need < 0:
+        raise ValueError("FA_ERR_BAD_SHAPE")
+    if workspace is None:
+        workspace = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    base = workspace.data_ptr()
+    ws = (base + 255) // 256 * 256
+    ws_size = workspace.numel() - (ws - base)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    _check_status(fa_bwd_raw(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, Sq, Sk, D, float(scale),
+        _mask_code(causal), _dtype_code(q.dtype), _dtype_code(dq.dtype), ws, ws_size, stream))
+    return dq, dk, dv
 
 
 def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,

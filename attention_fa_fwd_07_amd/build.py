@@ -10,7 +10,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "fa_fwd.hip")
+SRCS = [os.path.join(HERE, "csrc", f) for f in ("fa_fwd.hip", "fa_bwd.hip")]
 LIB = os.path.join(HERE, "libfa_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -35,7 +35,8 @@ def build(verbose: bool = False) -> str:
     """Compile the HIP library; returns the path of the .so. Always rebuilds."""
     inc = os.path.join(ROOT, "include")
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", inc, SRC, "-o", tmp]
+    srcs = [f for f in SRCS if os.path.exists(f)]
+    cmd = [HIPCC, *FLAGS, "-I", inc, *srcs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     log = os.path.join(HERE, "build.log")
     with open(log, "w") as f:

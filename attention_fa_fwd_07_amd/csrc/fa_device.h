@@ -1,0 +1,196 @@
+// Device helpers shared by the forward and backward kernels (gfx950):
+// MFMA and 16-bit packing wrappers, LDS swizzles, the HBM->LDS copy, wave
+// reductions, launch-order maps and barriers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <type_traits>
+
+namespace fa {
+
+
+enum Kind : int { KF16 = 0, KBF16 = 1, KFP8 = 2 };
+enum OutKind : int { OF16 = 0, OBF16 = 1, OF32 = 3 };
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_tr __attribute__((vector_size(8)));
+
+#define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
+
+template <typename T>
+__device__ __forceinline__ T bitcast(const u32x4& x) {
+  T r;
+  __builtin_memcpy(&r, &x, sizeof(T));
+  return r;
+}
+
+template <int KIND>
+__device__ __forceinline__ f32x16 mfma32(const u32x4& a, const u32x4& b, const f32x16& c) {
+  if constexpr (KIND == KBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(bitcast<bf16x8>(a), bitcast<bf16x8>(b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(bitcast<half8>(a), bitcast<half8>(b), c, 0, 0, 0);
+  }
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed 16-bit, round to nearest even (v_cvt_pk_{f16,bf16}_f32).
+template <int KIND>
+__device__ __forceinline__ uint32_t pack2(float x, float y) {
+  uint32_t u;
+  if constexpr (KIND == KBF16) {
+    const bf16x2_t v = {(__bf16)x, (__bf16)y};
+    __builtin_memcpy(&u, &v, 4);
+  } else {
+    const half2_t v = {(_Float16)x, (_Float16)y};
+    __builtin_memcpy(&u, &v, 4);
+  }
+  return u;
+}
+
+// acc + a.lo + a.hi for a packed pair of 16-bit values (v_dot2c_f32_*).
+template <int KIND>
+__device__ __forceinline__ float add_pair(uint32_t a, float acc) {
+  if constexpr (KIND == KBF16) {
+    bf16x2_t x, one = {(__bf16)1.0f, (__bf16)1.0f};
+    __builtin_memcpy(&x, &a, 4);
+    return __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+  } else {
+    half2_t x, one = {(_Float16)1.0f, (_Float16)1.0f};
+    __builtin_memcpy(&x, &a, 4);
+    return __builtin_amdgcn_fdot2(x, one, acc, false);
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ float unpack_lo(uint32_t x) {
+  uint16_t u = (uint16_t)(x & 0xffffu);
+  if constexpr (KIND == KBF16) {
+    return __uint_as_float((uint32_t)u << 16);
+  } else {
+    _Float16 h;
+    __builtin_memcpy(&h, &u, 2);
+    return (float)h;
+  }
+}
+
+template <int KIND>
+__device__ __forceinline__ float unpack_hi(uint32_t x) {
+  uint16_t u = (uint16_t)(x >> 16);
+  if constexpr (KIND == KBF16) {
+    return __uint_as_float((uint32_t)u << 16);
+  } else {
+    _Float16 h;
+    __builtin_memcpy(&h, &u, 2);
+    return (float)h;
+  }
+}
+
+// XOR swizzles of the 16-byte chunks of one LDS row (row r, chunk c is
+// stored at chunk c ^ swz(r)). They depend on the row pitch in bytes (RB:
+// 256 for 16-bit data at D=128, 128 for 16-bit at D=64 or fp8 at D=128, 64
+// for fp8 at D=64), because the pitch decides which rows share LDS banks.
+// The K swizzle spreads the 16 rows that one ds_read_b128 phase touches over
+// all 64 banks. The V swizzle for 16-bit data spreads the four rows that one
+// transposing read (ds_read_b64_tr_b16) touches over four different 64-byte
+// bank groups; fp8 V (ds_read_b64_tr_b8) uses the K pattern. Every swizzle
+// depends on the row index mod 16 only.
+template <int RB>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (RB == 256) return r & 15;
+  else if constexpr (RB == 128) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+template <int RB, bool TR8>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (TR8) return swz_k<RB>(r);
+  else if constexpr (RB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return ((r >> 1) & 1) << 2;
+}
+
+// 16 bytes per lane from base + voff (HBM) to LDS at lds_wave + 16 * lane
+// (global_load_lds_dwordx4). One asm statement sets M0 (the LDS destination,
+// wave-uniform), waits the one wait state the hardware needs between an M0
+// write and an LDS-DMA load, issues the load and restores M0, so the
+// compiler's view of M0 stays valid and it does not treat later LDS reads
+// as dependent on this load: the kernel waits for these loads explicitly
+// (s_waitcnt vmcnt) and orders them against LDS readers with barriers.
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_wave) {
+  uint32_t saved;
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(base), "s"(lds_wave)
+      : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ float wave_max_halves(float x) {
+  // After the swap each lane holds its own value and its partner's (l ^ 32).
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+}
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(p[0]) + __uint_as_float(p[1]);
+}
+
+// Map the launch-order workgroup id to a logical tile so that each XCD
+// (workgroups are dealt round-robin over the 8 XCDs) receives a contiguous
+// range of tiles: the query blocks of one head then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+  const int xcd = w & 7, local = w >> 3;
+  const int base = n >> 3, rem = n & 7;
+  return xcd * base + (xcd < rem ? xcd : rem) + local;
+}
+// The same with the launch order cut into groups of `unit` adjacent blocks
+// (the blocks of one head, or of the heads sharing one key/value head) dealt
+// round-robin to the XCDs: XCD x runs groups x, x+8, ... (needs n/unit to be
+// a multiple of 8). Used when the groups differ in work (variable lengths):
+// every XCD then gets a share of every sequence.
+__device__ __forceinline__ int xcd_deal(int w, int unit) {
+  const int xcd = w & 7, local = w >> 3;
+  const int g = local / unit;
+  return (xcd + 8 * g) * unit + (local - g * unit);
+}
+
+// Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
+// (lgkmcnt) but not for its HBM->LDS loads, which are waited for explicitly
+// (wait_loads) before the tile that reads them. The scheduling fences keep
+// the compiler from moving instructions across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// Wait until at most N of this wave's HBM->LDS loads are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_loads() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <typename T>
+__device__ __forceinline__ T lds_load(uint32_t addr) {
+  return *(const __attribute__((address_space(3))) T*)(uintptr_t)addr;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+}  // namespace fa

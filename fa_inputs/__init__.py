@@ -190,3 +190,11 @@ def make_varlen_inputs(lens_q, lens_k, H: int, Hkv: int, D: int, dtype: str, see
     cu_q = torch.tensor([0] + list(np.cumsum(lens_q)), dtype=torch.int32)
     cu_k = torch.tensor([0] + list(np.cumsum(lens_k)), dtype=torch.int32)
     return VarlenInputs(inp, cu_q, cu_k, int(max(lens_q)))
+
+
+def make_cotangent(shape, dtype: str, seed: int) -> torch.Tensor:
+    """Seeded gradient of the output for the backward pass: standard normal
+    float64 draws of ``shape`` cast to ``dtype`` as ``make_inputs`` does
+    (16-bit types only)."""
+    x = np.random.default_rng(seed).standard_normal(shape)
+    return torch.from_numpy(x).to(torch.float32).to(TORCH_DTYPE[dtype])

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 4
+#define FA_ABI_VERSION 5
 
 typedef enum {
   FA_OK = 0,
@@ -204,6 +204,39 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
                           float keep_prob, fa_dtype_t in_dtype, fa_dtype_t o_dtype,
                           const float* descale_q, const float* descale_k, const float* descale_v,
                           hipStream_t stream);
+
+/*
+ * Backward pass: the gradients of O = softmax(scale * Q K^T + mask) V for a
+ * cotangent dO, recomputing P from the forward's lse (the backward whose dQ
+ * pass "Hygon FlashAttention: fixed-defect review",
+ * chatdocs.ruinique.com/hygon/flash-attention-fixed-bugs, item 13,
+ * discusses; the formulas are the derivative of the forward):
+ *   dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale * dS K, dK = scale * dS^T Q,
+ * dK and dV of a key/value head summed over the query heads that share it
+ * (deterministic: no atomics).
+ *
+ * q, o, dout: [B, H, Sq, D] and k, v: [B, H_kv, Sk, D], contiguous BNSD, in
+ * in_dtype (FA_F16 or FA_BF16); lse: fp32 [B, H, Sq] as fa_fwd writes it (a
+ * row without a visible key: -inf). dq [B, H, Sq, D], dk, dv [B, H_kv, Sk, D]
+ * in grad_dtype (in_dtype or FA_F32), written whole. D 64 or 128; mask and
+ * scale as fa_fwd_ex. workspace: device memory of at least
+ * fa_bwd_workspace_size(B, H, Sq) bytes, 256-byte aligned, owned by the
+ * caller (per-row lse in log2 units and rowsum(dO * O)); contents on entry
+ * do not matter. Device pointers 16-byte aligned (lse: 4). Three kernels on
+ * `stream`. Errors as fa_fwd_ex (FA_ERR_WORKSPACE: missing or small
+ * workspace; FA_ERR_ALIASING: an output or the workspace overlaps another
+ * tensor).
+ */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D, float scale, fa_mask_t mask,
+                   fa_dtype_t in_dtype, fa_dtype_t grad_dtype, void* workspace,
+                   int64_t workspace_size, hipStream_t stream);
+
+/* Workspace bytes fa_bwd needs (8 bytes per query row, rows rounded up to a
+ * multiple of 32 per head); -1 for sizes it rejects. */
+int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq);
 
 /* Human-readable name of a status code ("FA_OK", ...); never NULL. */
 const char* fa_status_str(fa_status_t s);

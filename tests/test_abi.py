@@ -41,7 +41,7 @@ def test_library_holds_gfx950_code():
 
 def test_abi_version_and_status_strings():
     lib = fa.load_library()
-    assert lib.fa_abi_version() == 4
+    assert lib.fa_abi_version() == 5
     names = [fa.status_str(c) for c in range(13)]
     assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP" and names[11] == "FA_ERR_WORKSPACE"
     assert names[12] == "FA_ERR_UNSUPPORTED_MASK"
@@ -228,3 +228,49 @@ def test_varlen_wrapper_checks_offsets():
     cu = torch.tensor([0, 8], dtype=torch.int32)
     with pytest.raises(ValueError):
         fa.fa_fwd_varlen(x, x, x, cu, cu, 8)          # CPU tensors
+
+
+# ---- the backward entry point ----
+DO, GQ, GK, GV, WS = 0x80000000, 0x90000000, 0xA0000000, 0xB0000000, 0xC0000000
+
+
+def call_bwd(**over):
+    a = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=GQ, dk=GK, dv=GV, B=1, H=4, H_kv=2, Sq=100,
+             Sk=300, D=128, scale=0.125, mask=fa.FA_MASK_CAUSAL_BOTTOM_RIGHT,
+             in_dtype=fa.FA_F16, grad_dtype=fa.FA_F32, workspace=WS, workspace_size=1 << 20,
+             stream=None)
+    a.update(over)
+    return fa.fa_bwd_raw(**a)
+
+
+def test_bwd_workspace_size():
+    # lse2 and Delta, fp32, per query row; rows rounded up to 32 per head
+    assert fa.bwd_workspace_size(1, 4, 100) == 1 * 4 * 128 * 8
+    assert fa.bwd_workspace_size(2, 3, 64) == 2 * 3 * 64 * 8
+    for bad in ((0, 4, 100), (1, 0, 100), (1, 4, 0), (1 << 20, 1 << 10, 1 << 10)):
+        assert fa.bwd_workspace_size(*bad) == -1
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dout=None), fa.FA_ERR_NULL_POINTER),
+    (dict(lse=None), fa.FA_ERR_NULL_POINTER),
+    (dict(dv=None), fa.FA_ERR_NULL_POINTER),
+    (dict(H_kv=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(Sk=0), fa.FA_ERR_BAD_SHAPE),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(in_dtype=fa.FA_FP8_E4M3), fa.FA_ERR_UNSUPPORTED_DTYPE),
+    (dict(in_dtype=fa.FA_BF16, grad_dtype=fa.FA_F16), fa.FA_ERR_UNSUPPORTED_DTYPE),
+    (dict(mask=5), fa.FA_ERR_UNSUPPORTED_MASK),
+    (dict(scale=float("nan")), fa.FA_ERR_BAD_SCALE),
+    (dict(dq=GQ + 8), fa.FA_ERR_MISALIGNED),
+    (dict(lse=L + 2), fa.FA_ERR_MISALIGNED),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(workspace_size=100), fa.FA_ERR_WORKSPACE),
+    (dict(workspace=WS + 64), fa.FA_ERR_MISALIGNED),
+    (dict(dq=Q + 256), fa.FA_ERR_ALIASING),
+    (dict(dk=GQ + 1024), fa.FA_ERR_ALIASING),
+    (dict(workspace=GV), fa.FA_ERR_ALIASING),
+    (dict(dv=DO), fa.FA_ERR_ALIASING),
+])
+def test_bwd_rejects_before_launch(over, code):
+    assert call_bwd(**over) == code

@@ -1,0 +1,169 @@
+"""GPU parity of the backward pass (fa_bwd, through the C ABI) against the
+fp64 oracle's gradients.
+
+The kernels take O and lse as inputs. Here they are the oracle's forward
+results stored as the library stores them (O in the input type, lse fp32),
+so that the comparison measures the backward's own arithmetic; one test
+chains the library's forward instead.
+
+Tolerance: every product rounds one operand per term to the input type (P
+and dS in the MFMA inputs, O in rowsum(dO * O)) and sums in fp32, so the
+error of a gradient element is a small multiple of the unit roundoff u
+times the sum of the absolute values of its terms. The test bounds
+max |g - g_ref| over a tensor by 2u (fp16 u = 2^-11, bf16 2^-8: 9.8e-4 and
+7.8e-3) times the largest such sum over the tensor:
+  dQ: scale * (P * (|dP| + |Delta|)) |K|,  dK: scale * (P * (|dP| + |Delta|))^T |Q|,
+  dV: P^T |dO|
+(never below max |g_ref|; unlike max |g_ref| it does not vanish where the
+terms cancel, e.g. one key: dS = dP - Delta = 0).
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_fa_fwd_07_amd as fa
+import fa_inputs as fi
+from oracle import attention_bwd_fp64, attention_fp64, head_forward
+
+pytestmark = pytest.mark.gpu
+
+TOL = {fi.F16: 2 * 2.0 ** -11, fi.BF16: 2 * 2.0 ** -8}
+MASKS = {"none": (False, 0), "top_left": (True, 0), "bottom_right": (True, None)}
+
+
+def case_inputs(dtype, B, H, Hkv, Sq, Sk, D, seed, amp=1.0):
+    cfg = fi.Config("bwd", B, H, Sq, Sk, D, dtype, False, seed=seed, amp=amp)
+    inp = fi.make_inputs(cfg)
+    inp.k = inp.k[:, :Hkv].contiguous()
+    inp.v = inp.v[:, :Hkv].contiguous()
+    do = fi.make_cotangent((B, H, Sq, D), dtype, seed + 5000)
+    return cfg, inp, do
+
+
+def term_bounds(q, k, v, g, scale, causal, off):
+    """Largest sum of absolute term values per gradient tensor."""
+    B, H, Sq, D = q.shape
+    Hkv = k.shape[1]
+    bq = 0.0
+    bk = np.zeros(k.shape)
+    bv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            kv = h // (H // Hkv)
+            _, _, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal, return_p=True,
+                                   offset=off)
+            dp = g[b, h] @ v[b, kv].T
+            w = p * (np.abs(dp) + np.abs(np.sum(p * dp, axis=1, keepdims=True)))
+            bq = max(bq, float(np.max(abs(scale) * w @ np.abs(k[b, kv]))))
+            bk[b, kv] += abs(scale) * w.T @ np.abs(q[b, h])
+            bv[b, kv] += p.T @ np.abs(g[b, h])
+    return bq, float(bk.max()), float(bv.max())
+
+
+def oracle_all(cfg, inp, do, causal, off):
+    q, k, v = fi.values(inp)
+    g = do.double().numpy()
+    o, lse = attention_fp64(q, k, v, cfg.scale, causal, off)
+    dq, dk, dv = attention_bwd_fp64(q, k, v, g, cfg.scale, causal, off)
+    bounds = term_bounds(q, k, v, g, cfg.scale, causal, off)
+    return o, lse, (dq, dk, dv), bounds
+
+
+def run_bwd(cfg, inp, do, o, lse, causal, grad_dtype):
+    td = fi.TORCH_DTYPE[cfg.dtype]
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    ot = torch.from_numpy(o).to(torch.float32).to(td).cuda()
+    lt = torch.from_numpy(lse).to(torch.float32).cuda()
+    gd = fi.TORCH_DTYPE[grad_dtype]
+    dq = torch.full(tuple(q.shape), float("nan"), dtype=gd, device="cuda")
+    dk = torch.full(tuple(k.shape), float("nan"), dtype=gd, device="cuda")
+    dv = torch.full(tuple(v.shape), float("nan"), dtype=gd, device="cuda")
+    ws = torch.full((fa.bwd_workspace_size(cfg.B, cfg.H, cfg.Sq) + 256,), 255, dtype=torch.uint8,
+                    device="cuda")
+    fa.fa_bwd(q, k, v, ot, do.cuda(), lt, scale=cfg.scale, causal=causal, dq=dq, dk=dk, dv=dv,
+              workspace=ws)
+    torch.cuda.synchronize()
+    return tuple(t.double().cpu().numpy() for t in (dq, dk, dv))
+
+
+def check(dtype, got, ref, bounds, what):
+    errs = []
+    for name, g, r, bnd in zip(("dq", "dk", "dv"), got, ref, bounds):
+        assert np.all(np.isfinite(g)), f"{what}: non-finite {name}"
+        scale = max(bnd, np.max(np.abs(r)), 1e-30)
+        e = np.max(np.abs(g - r)) / scale
+        errs.append(e)
+        assert e <= TOL[dtype], f"{what}: {name} rel err {e:.3e} (tol {TOL[dtype]:.2e})"
+    return errs
+
+
+LENGTHS = [(1, 1), (33, 65), (64, 64), (65, 130), (130, 65), (200, 200), (257, 129)]
+
+
+@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_bwd_edge_sweep(dtype, D, mask):
+    worst = [0.0, 0.0, 0.0]
+    for i, (Sq, Sk) in enumerate(LENGTHS):
+        H, Hkv = ((2, 2), (4, 2), (3, 1))[i % 3]
+        causal = MASKS[mask][0]
+        off = (Sk - Sq) if mask == "bottom_right" else 0
+        cfg, inp, do = case_inputs(dtype, 1, H, Hkv, Sq, Sk, D, seed=1400 + 13 * i + D)
+        o, lse, ref, bnd = oracle_all(cfg, inp, do, causal, off)
+        causal_arg = False if mask == "none" else mask
+        for gd in (fi.F32, dtype):
+            got = run_bwd(cfg, inp, do, o, lse, causal_arg, gd)
+            e = check(dtype, got, ref, bnd, f"{dtype} D{D} {mask} {Sq}x{Sk} H{H}/{Hkv} {gd}")
+            if gd == fi.F32:
+                worst = [max(a, b) for a, b in zip(worst, e)]
+    print(f"{dtype} D{D} {mask}: worst rel err dq/dk/dv {worst}")
+
+
+@pytest.mark.parametrize("dtype,D,mask,H,Hkv,S", [
+    (fi.F16, 128, "none", 4, 4, 4096),
+    (fi.BF16, 128, "top_left", 4, 2, 2048),
+    (fi.F16, 64, "bottom_right", 3, 1, 1500),
+])
+def test_bwd_long_sequences(dtype, D, mask, H, Hkv, S):
+    """Long rows: whole heads of 1500..4096 tokens against the oracle."""
+    causal = MASKS[mask][0]
+    Sk = S if mask != "bottom_right" else S + 300
+    cfg, inp, do = case_inputs(dtype, 1, H, Hkv, S, Sk, D, seed=1450 + D + H)
+    off = (Sk - S) if mask == "bottom_right" else 0
+    o, lse, ref, bnd = oracle_all(cfg, inp, do, causal, off)
+    got = run_bwd(cfg, inp, do, o, lse, False if mask == "none" else mask, fi.F32)
+    e = check(dtype, got, ref, bnd, f"long {dtype} D{D} {mask} S{S}")
+    print(f"long {dtype} D{D} {mask} S{S}: rel err dq/dk/dv {e}")
+
+
+def test_bwd_chained_with_library_forward():
+    """fa_fwd's own O and lse feed fa_bwd (the training-step order)."""
+    for dtype in (fi.F16, fi.BF16):
+        cfg, inp, do = case_inputs(dtype, 2, 4, 2, 300, 300, 128, seed=1470)
+        q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+        o, lse = fa.fa_fwd(q, k, v, scale=cfg.scale, causal=True)
+        dq, dk, dv = fa.fa_bwd(q, k, v, o, do.cuda(), lse, scale=cfg.scale, causal=True,
+                               grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        _, _, ref, bnd = oracle_all(cfg, inp, do, True, 0)
+        check(dtype, tuple(t.double().cpu().numpy() for t in (dq, dk, dv)), ref, bnd,
+              f"chained {dtype}")
+
+
+def test_bwd_deterministic():
+    cfg, inp, do = case_inputs(fi.F16, 2, 8, 2, 700, 700, 128, seed=1480)
+    o, lse, _, _ = oracle_all(cfg, inp, do, True, 0)
+    a = run_bwd(cfg, inp, do, o, lse, True, fi.F16)
+    b = run_bwd(cfg, inp, do, o, lse, True, fi.F16)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_bwd_large_logits():
+    """Scores far past the fp16 exp-overflow point (amplitude 3 at D=64)."""
+    cfg, inp, do = case_inputs(fi.F16, 1, 2, 2, 300, 300, 64, seed=1490, amp=3.0)
+    o, lse, ref, bnd = oracle_all(cfg, inp, do, True, 0)
+    got = run_bwd(cfg, inp, do, o, lse, True, fi.F32)
+    e = check(fi.F16, got, ref, bnd, "large logits")
+    print(f"large logits: rel err dq/dk/dv {e}")
