@@ -2,11 +2,15 @@
 MFMA peak on B4 H32 Sq=Sk=4096 D128 fp16, BNSD, non-causal, one GPU.
 
 One step = one fa_fwd call over the whole batch (inputs resident in HBM).
-Prints one JSON line. Options:
+With --pass bwd one step is one fa_bwd call (dQ, dK, dV from the forward's
+O and lse, which are computed before the timed region) on the same
+workload, counted at 2.5 times the forward's flop. Prints one JSON line.
+Options:
   --gpus N      only N=1 is supported (one process, one GPU)
   --steps K     timed steps (default 50)
   --warmup W    untimed steps first (default 30: the clocks settle under load)
   --workload I  index into the workload list (default: the headline, 2)
+  --pass P      fwd (default) or bwd
   --no-cpu      skip the CPU-oracle baseline leg
   --cpu-seconds approximate CPU budget for the oracle leg (default 15)
 """
@@ -26,11 +30,15 @@ sys.path.insert(0, ROOT)
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8_e4m3": 5033.2}   # dense MFMA, MI355X
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_b4h32s4096d128_f16_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "attention_fa_fwd_07_amd", "csrc", "fa_fwd.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "attention_fa_fwd_07_amd", "csrc", f)
+               for f in ("fa_fwd.hip", "fa_device.h")]
 
 
 def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def device_info():
@@ -91,12 +99,43 @@ def cpu_baseline(cfg, inp, budget_s: float):
                       f"{dt:.1f} s; value = algorithmic FLOP of the sample / wall time"}
 
 
+def cpu_baseline_bwd(cfg, inp, dout, budget_s: float):
+    """The oracle's backward, as it stands, on a bounded sample of whole heads."""
+    import fa_inputs as fi
+    from oracle import attention_bwd_fp64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    heads = 0
+    t0 = time.perf_counter()
+    bh = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    while heads < len(bh):
+        b, h = bh[heads]
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        q = fi.as_float64(inp.q[sl], inp.descale_q)
+        k = fi.as_float64(inp.k[sl], inp.descale_k)
+        v = fi.as_float64(inp.v[sl], inp.descale_v)
+        attention_bwd_fp64(q, k, v, dout[sl].double().numpy(), cfg.scale, cfg.causal)
+        heads += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 2.5 * cfg.flops() * heads / (cfg.B * cfg.H)
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"backward of {heads} of {cfg.B * cfg.H} heads of {cfg.name}, fp64 numpy, "
+                      f"{dt:.1f} s; value = 2.5 x forward flop of the sample / wall time"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -133,9 +172,24 @@ def main():
                ("descale_v", inp.descale_v))}
     o = torch.empty(tuple(q.shape), dtype=fi.TORCH_DTYPE[cfg.o_dtype], device=dev)
     lse = torch.empty(tuple(q.shape[:3]), dtype=torch.float32, device=dev)
+    bwd = args.which == "bwd"
+    if bwd:
+        if cfg.dtype not in (fi.F16, fi.BF16):
+            print("the backward takes fp16 or bf16 inputs", file=sys.stderr)
+            sys.exit(2)
+        dout_cpu = fi.make_cotangent(tuple(q.shape), cfg.dtype, cfg.seed + 5000)
+        dout = dout_cpu.to(dev)
+        fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
+        grads = tuple(torch.empty_like(t) for t in (q, k, v))
+        ws = torch.empty(fa.bwd_workspace_size(cfg.B, cfg.H, cfg.Sq) + 256, dtype=torch.uint8,
+                         device=dev)
 
     def step():
-        fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse, **kw)
+        if bwd:
+            fa.fa_bwd(q, k, v, o, dout, lse, scale=cfg.scale, causal=cfg.causal, dq=grads[0],
+                      dk=grads[1], dv=grads[2], workspace=ws)
+        else:
+            fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse, **kw)
 
     for _ in range(args.warmup):
         step()
@@ -157,18 +211,21 @@ def main():
     med_ms = statistics.median(per_launch_ms)
     ms_per_step = wall / args.steps * 1e3
 
-    flops = cfg.flops()
+    flops = cfg.flops() * (2.5 if bwd else 1.0)
     value = flops / (ms_per_step * 1e-3) / 1e12
     peak = PEAK_TFLOPS[cfg.dtype]
     achieved = flops / (avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": measured_traffic(),
-                "kernel": "fa_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
+                "traffic": None if bwd else measured_traffic(),
+                "kernel": "fa_bwd (row pass, dK/dV and dQ kernels; one call)" if bwd
+                else "fa_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
                 "median_launch_ms": round(med_ms, 4), "min_launch_ms": round(min(per_launch_ms), 4)}
 
     out = {
-        "metric": "attn fwd TFLOP/s + % fp16 MFMA peak, B4 H32 S4096 D128 fp16 (1 GPU)",
+        "metric": ("attn bwd TFLOP/s (2.5x forward flop) + % fp16 MFMA peak, "
+                   f"{cfg.name} (1 GPU)") if bwd else
+                  "attn fwd TFLOP/s + % fp16 MFMA peak, B4 H32 S4096 D128 fp16 (1 GPU)",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "pct_peak": round(100 * value / peak, 2),
@@ -183,12 +240,14 @@ def main():
         "data": "synthetic (seeded N(0,1), BNSD)",
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Sq": cfg.Sq, "Sk": cfg.Sk,
                    "D": cfg.D, "causal": cfg.causal, "in_dtype": cfg.dtype,
-                   "o_dtype": cfg.o_dtype, "layout": "BNSD", "flop_per_step": flops},
+                   "o_dtype": cfg.o_dtype, "layout": "BNSD", "flop_per_step": flops,
+                   "pass": args.which},
         "roofline": roofline,
         "device": device_info(),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        out["cpu_baseline"] = (cpu_baseline_bwd(cfg, inp, dout_cpu, args.cpu_seconds) if bwd
+                               else cpu_baseline(cfg, inp, args.cpu_seconds))
     print(json.dumps(out), flush=True)
 
 
