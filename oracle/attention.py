@@ -49,6 +49,20 @@ pages mention the backward's dQ pass only for a stride defect ("Hygon
 FlashAttention: fixed-defect review", item 13) and state none of its
 formulas; these are the derivative of the forward definition.
 
+Dropout (``attention_dropout_fp64``): the pages pass a keep probability
+through the call ("Tracing npu_flash_attention through the CANN runtime",
+layer 1: keep_prob) and never define it. The reading adopted is inverted
+dropout on the normalised probabilities: O = (P * Z / keep_prob) V with Z a
+0/1 mask, P the softmax over all visible keys (so lse is unchanged). Z comes
+from the counter-based generator Philox4x64-10 (Salmon, Moraes, Dror and
+Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011), taken here
+from numpy's implementation (numpy.random.Philox), keyed by (seed, offset):
+for query head index bh = b*H + h, query row i, 32-key tile t and half
+u in {0, 1}, the counter (2t + u, i, bh, 0) gives four 64-bit words w0..w3,
+read as sixteen 16-bit values v_n = (w_{n/4} >> 16*(n%4)) & 0xffff; key
+32t + 8m + 4u + e (m, e in 0..3) takes v_{4m+e} and is kept iff it is below
+thr = round(keep_prob * 65536) (clamped to 1..65535).
+
 Everything is float64 from the exact input values. S and P are
 materialised per (batch, head).
 
@@ -183,6 +197,57 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
             dq[b, h] = scale * (ds @ np.asarray(k[b, kv], np.float64))  # dQ = scale dS K
             dk[b, kv] += scale * (ds.T @ np.asarray(q[b, h], np.float64))   # dK = scale dS^T Q
     return dq, dk, dv
+
+
+def dropout_threshold(keep_prob: float) -> int:
+    """16-bit threshold of the keep test (a value below it is kept)."""
+    if not (0.0 < keep_prob < 1.0):
+        raise ValueError("keep_prob must lie in (0, 1)")
+    return min(max(int(round(keep_prob * 65536.0)), 1), 65535)
+
+
+def dropout_keep_mask(bh: int, rows, Sk: int, keep_prob: float, seed: int, rng_offset: int):
+    """Z [len(rows), Sk] (0/1) for query head index bh, by the rule above."""
+    thr = dropout_threshold(keep_prob)
+    nblk = 2 * ((Sk + 31) // 32)                  # counters 2t + u of one row
+    key = np.array([seed, rng_offset], dtype=np.uint64)
+    z = np.zeros((len(rows), nblk * 16), np.float64)
+    for r, i in enumerate(rows):
+        # numpy's Philox adds one to the 256-bit counter before each block:
+        # start one below (0, i, bh, 0) to get the blocks 0, 1, 2, ...
+        c = (int(i) << 64) + (int(bh) << 128) - 1
+        ctr = np.array([(c >> (64 * w)) & ((1 << 64) - 1) for w in range(4)], dtype=np.uint64)
+        words = np.random.Philox(key=key, counter=ctr).random_raw(4 * nblk).astype(np.uint64)
+        v = np.stack([(words >> np.uint64(16 * s)) & np.uint64(0xffff) for s in range(4)],
+                     axis=1).reshape(nblk, 16)      # v[block, n]
+        # block 2t + u, value n = 4m + e  ->  key 32t + 8m + 4u + e
+        t, u = np.divmod(np.arange(nblk), 2)
+        m, e = np.divmod(np.arange(16), 4)
+        keys = 32 * t[:, None] + 8 * m[None, :] + 4 * u[:, None] + e[None, :]
+        z[r, keys.ravel()] = (v.ravel() < thr).astype(np.float64)
+    return z[:, :Sk]
+
+
+def attention_dropout_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,
+                           causal: bool, offset: int, keep_prob: float, seed: int,
+                           rng_offset: int = 0, rows=None):
+    """Forward with dropout over BNSD tensors (see above): O [B,H,R,D] and
+    the (undropped) lse [B,H,R] for the query rows ``rows`` (all by default)."""
+    group = _check(q, k, v)
+    B, H, Sq, D = q.shape
+    Sk = k.shape[2]
+    rows = np.arange(Sq) if rows is None else np.asarray(rows, np.int64)
+    o = np.empty((B, H, len(rows), D))
+    lse = np.empty((B, H, len(rows)))
+    for b in range(B):
+        for h in range(H):
+            kv = h // group
+            _, l, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal, rows=rows,
+                                   return_p=True, offset=offset)
+            z = dropout_keep_mask(b * H + h, rows, Sk, keep_prob, seed, rng_offset)
+            o[b, h] = (p * z / keep_prob) @ np.asarray(v[b, kv], np.float64)
+            lse[b, h] = l
+    return o, lse
 
 
 def attention_rows_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float,

@@ -15,8 +15,9 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import (attention_bruteforce, attention_bwd_fp64, attention_fp64,
-                    attention_rows_fp64, attention_varlen_fp64, head_forward)
+from oracle import (attention_bruteforce, attention_bwd_fp64, attention_dropout_fp64,
+                    attention_fp64, attention_rows_fp64, attention_varlen_fp64,
+                    dropout_keep_mask, dropout_threshold, head_forward)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_facts.json")
 
@@ -769,3 +770,179 @@ def test_backward_pins_accept_correct_copy():
     fn = _bmutant("none")
     for pin in BPINS:
         pin(fn)
+
+
+# -------------------------------------------------------- dropout pins ----
+# fn(q, k, v, scale, causal, offset, keep, seed, rng_offset) -> (O, lse) and
+# mfn(bh, rows, Sk, keep, seed, rng_offset) -> Z: the forward with dropout
+# and its keep mask.
+
+_M64 = (1 << 64) - 1
+
+
+def philox4x64_10(ctr, key):
+    """Philox4x64-10 written out from its published definition (Salmon et
+    al., SC 2011): ten rounds of two 64x64->128-bit products with the round
+    multipliers, the key bumped by the Weyl constants between rounds."""
+    c = list(ctr)
+    k0, k1 = key
+    for r in range(10):
+        if r:
+            k0 = (k0 + 0x9E3779B97F4A7C15) & _M64
+            k1 = (k1 + 0xBB67AE8584CAA73B) & _M64
+        p0 = 0xD2E7470EE14C6C93 * c[0]
+        p1 = 0xCA5A826395121157 * c[2]
+        c = [(p1 >> 64) ^ c[1] ^ k0, p1 & _M64, (p0 >> 64) ^ c[3] ^ k1, p0 & _M64]
+    return c
+
+
+def dpin_bits_bruteforce(fn, mfn):
+    """Every keep bit against the pure-Python Philox, element by element
+    (query heads and rows 0 and large, keys across several tiles and a
+    ragged tail)."""
+    for (bh, rows, Sk, keep, seed, off) in [(0, [0, 1, 2], 70, 0.8, 0, 0),
+                                            (5, [31, 4096], 40, 0.5, 123456789, 3),
+                                            (77, [7], 97, 0.1, (1 << 64) - 1, (1 << 63) + 5)]:
+        z = mfn(bh, rows, Sk, keep, seed, off)
+        thr = min(max(int(round(keep * 65536)), 1), 65535)
+        for r, i in enumerate(rows):
+            for j in range(Sk):
+                t, o32 = divmod(j, 32)
+                u, m, e = (o32 >> 2) & 1, o32 >> 3, o32 & 3
+                w = philox4x64_10((2 * t + u, i, bh, 0), (seed, off))
+                n = 4 * m + e
+                val = (w[n // 4] >> (16 * (n % 4))) & 0xffff
+                assert z[r, j] == (1.0 if val < thr else 0.0), (bh, i, j)
+
+
+def dpin_keep_fraction(fn, mfn):
+    """The kept fraction over 2^18 draws is thr / 65536 within 5 sigma."""
+    for keep in (0.9, 0.5, 0.13):
+        z = mfn(3, range(64), 4096, keep, 99, 1)
+        p = dropout_threshold(keep) / 65536.0
+        sig = math.sqrt(p * (1 - p) / z.size)
+        assert abs(z.mean() - p) <= 5 * sig, (keep, z.mean())
+
+
+def dpin_unbiased(fn, mfn):
+    """The mean of O over many seeds is the undropped O (pure-Python loops)
+    within 5 standard errors."""
+    q = rand((1, 1, 3, 2), 91)
+    k = rand((1, 1, 5, 2), 92)
+    v = rand((1, 1, 5, 2), 93)
+    ref, _ = attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), 0.9, True, 1)
+    ref = np.asarray(ref)
+    outs = np.stack([fn(q, k, v, 0.9, True, 1, 0.6, s, 0)[0] for s in range(600)])
+    se = outs.std(axis=0) / math.sqrt(len(outs))
+    assert np.all(np.abs(outs.mean(axis=0) - ref) <= 5 * se + 1e-12)
+
+
+def dpin_lse_undropped(fn, mfn):
+    """lse is the logsumexp of all visible scaled scores (torch.logsumexp)."""
+    q = rand((1, 2, 6, 4), 95)
+    k = rand((1, 2, 9, 4), 96)
+    v = rand((1, 2, 9, 4), 97)
+    _, lse = fn(q, k, v, 0.7, True, 2, 0.3, 5, 0)
+    s = torch.from_numpy(q) @ torch.from_numpy(k).transpose(-1, -2) * 0.7
+    keep = torch.arange(9)[None, :] <= torch.arange(6)[:, None] + 2
+    ref = torch.logsumexp(s.masked_fill(~keep, -math.inf), dim=-1).numpy()
+    assert np.max(np.abs(lse - ref)) <= 1e-12
+
+
+def dpin_streams_differ(fn, mfn):
+    """Masks of other heads, rows, seeds and offsets are different draws."""
+    base = mfn(4, [10], 256, 0.5, 1, 2)
+    for other in (mfn(5, [10], 256, 0.5, 1, 2), mfn(4, [11], 256, 0.5, 1, 2),
+                  mfn(4, [10], 256, 0.5, 2, 2), mfn(4, [10], 256, 0.5, 1, 3)):
+        assert np.mean(other != base) > 0.3
+
+
+def dpin_threshold_edge(fn, mfn):
+    """A value equal to the threshold is dropped, one below it kept: the
+    keep probability is chosen so that the threshold equals the value drawn
+    for key 0 of row 0 (pure-Python Philox)."""
+    for seed in (11, 12, 13):
+        w = philox4x64_10((0, 0, 0, 0), (seed, 0))
+        v0 = w[0] & 0xffff
+        if not 2 <= v0 <= 65534:
+            continue
+        assert mfn(0, [0], 4, v0 / 65536.0, seed, 0)[0, 0] == 0.0
+        assert mfn(0, [0], 4, (v0 + 1) / 65536.0, seed, 0)[0, 0] == 1.0
+
+
+DPINS = [dpin_bits_bruteforce, dpin_keep_fraction, dpin_unbiased, dpin_lse_undropped,
+         dpin_streams_differ, dpin_threshold_edge]
+
+
+@pytest.mark.parametrize("pin", DPINS, ids=lambda p: p.__name__)
+def test_oracle_dropout_pin(pin):
+    pin(lambda q, k, v, sc, c, off, kp, seed, ro: attention_dropout_fp64(q, k, v, sc, c, off, kp,
+                                                                         seed, ro),
+        dropout_keep_mask)
+
+
+def _dmutant(kind):
+    """Independent scaffold (pure-Python Philox) with one planted mistake
+    per kind ("none": correct)."""
+    def mfn(bh, rows, Sk, keep, seed, off):
+        thr = min(max(int(round(keep * 65536)), 1), 65535)
+        z = np.zeros((len(rows), Sk))
+        for r, i in enumerate(rows):
+            cache = {}
+            for j in range(Sk):
+                t, o32 = divmod(j, 32)
+                u, m, e = (o32 >> 2) & 1, o32 >> 3, o32 & 3
+                ctr = (2 * t + u, i, 0 if kind == "head_ignored" else bh, 0)
+                if ctr not in cache:
+                    cache[ctr] = philox4x64_10(ctr, (seed, off))
+                w = cache[ctr]
+                n = 4 * m + e
+                wi = 3 - n // 4 if kind == "word_order" else n // 4
+                val = (w[wi] >> (16 * (n % 4))) & 0xffff
+                kept = val <= thr if kind == "keep_le" else val < thr
+                z[r, j] = 1.0 if kept else 0.0
+        return z
+
+    def fn(q, k, v, scale, causal, offset, keep, seed, ro):
+        B, H, Sq, D = q.shape
+        Sk = k.shape[2]
+        o = np.zeros((B, H, Sq, D))
+        lse = np.zeros((B, H, Sq))
+        for b in range(B):
+            for h in range(H):
+                s = q[b, h] @ k[b, h].T * scale
+                if causal:
+                    s = np.where(np.arange(Sk)[None, :] > np.arange(Sq)[:, None] + offset, -np.inf, s)
+                mx = s.max(axis=1, keepdims=True)
+                p = np.exp(s - mx)
+                p /= p.sum(axis=1, keepdims=True)
+                z = mfn(b * H + h, range(Sq), Sk, keep, seed, ro)
+                pd = p * z
+                o[b, h] = (pd if kind == "no_rescale" else pd / keep) @ v[b, h]
+                ex = np.exp(s - mx) * (z if kind == "lse_dropped" else 1.0)
+                with np.errstate(divide="ignore"):
+                    lse[b, h] = mx[:, 0] + np.log(ex.sum(axis=1))
+        return o, lse
+    return fn, mfn
+
+
+DMUTANTS = ["head_ignored", "word_order", "keep_le", "no_rescale", "lse_dropped"]
+
+
+@pytest.mark.parametrize("kind", DMUTANTS)
+def test_dropout_pins_catch_planted_mistakes(kind):
+    fn, mfn = _dmutant(kind)
+    failed = []
+    for pin in DPINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(fn, mfn)
+        except (AssertionError, ValueError, FloatingPointError):
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches the planted mistake {kind!r}"
+
+
+def test_dropout_pins_accept_correct_copy():
+    fn, mfn = _dmutant("none")
+    for pin in DPINS:
+        pin(fn, mfn)
