@@ -35,7 +35,7 @@ FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL_TOP_LEFT, FA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-           "fa_fwd_varlen", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
+           "fa_fwd_varlen", "fa_fwd_dropout", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
            "fa_abi_version")
 
 _lib = None
@@ -75,6 +75,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                   i64, i64, i64, i64, i64, i64, i64,  # B H H_kv tq tk maxq D
                                   ctypes.c_float, ctypes.c_int, ctypes.c_float,
                                   ctypes.c_int, ctypes.c_int, vp, vp, vp, vp]
+    lib.fa_fwd_dropout.restype = ctypes.c_int
+    lib.fa_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
+                                   ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
+                                   ctypes.c_uint64, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                   vp, vp, vp, vp]
     lib.fa_bwd.restype = ctypes.c_int
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp,          # q k v o dout lse
                            vp, vp, vp,                      # dq dk dv
@@ -136,6 +141,15 @@ def fa_fwd_varlen_raw(q, k, v, o, lse, cu_q, cu_k, B, H, H_kv, total_q, total_k,
                                         stream)
 
 
+def fa_fwd_dropout_raw(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask, keep_prob,
+                       seed, offset, in_dtype, o_dtype, descale_q, descale_k, descale_v,
+                       stream) -> int:
+    """The dropout C entry point with integer pointers; returns the status code."""
+    return load_library().fa_fwd_dropout(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale,
+                                         mask, keep_prob, seed, offset, in_dtype, o_dtype,
+                                         descale_q, descale_k, descale_v, stream)
+
+
 def fa_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D, scale, mask,
                in_dtype, grad_dtype, workspace, workspace_size, stream) -> int:
     """The backward C entry point with integer pointers; returns the status code."""
@@ -175,7 +189,8 @@ def _check_status(code: int) -> None:
 
 def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
            keep_prob: float = 1.0, o_dtype=None, descale_q=None, descale_k=None,
-           descale_v=None, out=None, lse=None, stream=None, layout: str = "BNSD"):
+           descale_v=None, out=None, lse=None, stream=None, layout: str = "BNSD",
+           seed: int | None = None, rng_offset: int = 0):
     """Attention forward over BNSD tensors on the GPU.
 
     q [B,H,Sq,D], k/v [B,H_kv,Sk,D] contiguous GPU tensors (fp16, bf16 or
@@ -187,7 +202,15 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
     tensors (value = code * descale). Returns (o, lse): o [B,H,Sq,D] in
     ``o_dtype`` (default: fp16 for fp16/fp8 inputs, bf16 for bf16 inputs),
     lse [B,H,Sq] fp32 (natural-log logsumexp of the scaled, masked scores).
+    ``keep_prob`` < 1 applies dropout (fa_fwd_dropout) with the mask drawn
+    from ``seed`` (required then) and ``rng_offset``.
     """
+    if keep_prob != 1.0:
+        if seed is None:
+            raise ValueError("dropout (keep_prob < 1) needs a seed")
+        return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k,
+                     descale_v, out, lse, stream, None, None, layout,
+                     dropout=(int(seed), int(rng_offset)))
     return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
                  out, lse, stream, None, None, layout)
 
@@ -327,7 +350,7 @@ def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = 
 
 
 def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
-          out, lse, stream, num_splits, workspace, layout="BNSD"):
+          out, lse, stream, num_splits, workspace, layout="BNSD", dropout=None):
     import torch
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_cuda:
@@ -370,6 +393,11 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
         stream = torch.cuda.current_stream(dev).cuda_stream
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
     tail = (float(keep_prob), in_code, _dtype_code(out.dtype), dq, dk, dv)
+    if dropout is not None:
+        _check_status(fa_fwd_dropout_raw(*ptrs, B, H, Hkv, Sq, Sk, D, lay, float(scale), mask,
+                                         float(keep_prob), dropout[0] & ((1 << 64) - 1),
+                                         dropout[1] & ((1 << 64) - 1), *tail[1:], stream))
+        return out, lse
     general = Hkv != H or mask == FA_MASK_CAUSAL_BOTTOM_RIGHT or lay != FA_LAYOUT_BNSD
     args = ptrs + (B, H, Sq, Sk, D, FA_LAYOUT_BNSD, float(scale), 1 if mask else 0) + tail
     if num_splits is None and not general:

@@ -77,6 +77,11 @@ struct Params {
   const int32_t* cu_k;
   int32_t br;
   int32_t xcd_unit;     // > 0: launch-order groups dealt round-robin to the XCDs
+  // dropout: the keep test of key j for query row i of query head bh uses
+  // Philox4x64-10 keyed by (seed, rng_off); a kept P is scaled by inv_keep
+  uint64_t seed, rng_off;
+  uint32_t keep_thr;    // a 16-bit draw below this keeps its P
+  float inv_keep;
   float scale_log2;     // |scale| * log2(e)
   int32_t negate;       // scale < 0: Q fragments are negated (exact)
   // split-KV only: key-tile ranges per query block, partial results
@@ -85,6 +90,30 @@ struct Params {
   float* ws_lse;        // [nsplit][B*H*Sq] fp32, lse of each range (-inf: no key)
 };
 
+
+// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+// as easy as 1, 2, 3", SC 2011): ten rounds, each taking the two 128-bit
+// products of counter words 0 and 2 with the round multipliers and mixing
+// their halves with words 1 and 3 and the key; the key advances by the two
+// Weyl constants between rounds. c is the counter on entry, the output on
+// return.
+__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
+    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    c[0] = hi1 ^ c[1] ^ k0;
+    c[1] = lo1;
+    c[2] = hi0 ^ c[3] ^ k1;
+    c[3] = lo0;
+  }
+}
 
 // One workgroup: NW waves, BM = 32 * NW query rows, 32 per wave.
 // Keys and values stream through LDS in tiles of BN rows, in a ring of NB
@@ -101,7 +130,15 @@ struct Params {
 // for fp16 inputs, and the V codes, read transposed from LDS with
 // ds_read_b64_tr_b8, are converted exactly to fp16 (every e4m3fn value is
 // an fp16 value); the descale of V multiplies O in the epilogue.
-template <int D, int BN_, int NW_, int NB_, bool CAUSAL, int KIND, int OUT, bool SPLIT>
+//
+// Dropout (DROP): P is computed and summed into l as without it; the P
+// multiplied by V has each dropped entry set to 0, and the epilogue scales O
+// by 1/keep_prob. The keep test of the 16 keys a lane holds in a 32-key tile
+// j (registers r = 0..15: key 32j + 8*(r/4) + 4*hl + r%4) uses one Philox
+// call with counter (2j + hl, query row, b*H + h, 0): 16-bit value r of the
+// output (bits 16r .. 16r+15, word 0 lowest) below keep_thr keeps key r.
+template <int D, int BN_, int NW_, int NB_, bool CAUSAL, int KIND, int OUT, bool SPLIT,
+          bool DROP = false>
 struct FwdTile {
   static constexpr bool F8 = (KIND == KFP8);
   static constexpr int MK = F8 ? KF16 : KIND;     // type of the P.V product
@@ -126,6 +163,7 @@ struct FwdTile {
   static_assert(NB >= 2 && (NB - 2) * 2 * LOADS < 64, "ring depth: the loads in flight must fit the vmcnt field");
   static_assert(NCH % 64 == 0 && NCH % NT == 0 && (NT & (NT - 1)) == 0, "tile must split evenly over the lanes");
   static_assert((NT / C) % 16 == 0, "swizzle period must divide the rows per load");
+  static_assert(!DROP || (NKB == 1 && !SPLIT), "dropout: one 32-key block per tile, no split");
 
   typedef typename std::conditional<F8, i32x8, u32x4>::type qfrag_t;
 
@@ -475,7 +513,20 @@ struct FwdTile {
     }
   }
 
-  __device__ __forceinline__ void exp_p(const f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1]) {
+  // keep masks of this lane's 8 register pairs for tile j: value pair
+  // (2q, 2q+1) is the q-th 32-bit half of the Philox output
+  __device__ __forceinline__ void drop_masks(int j, uint32_t (&dm)[8]) {
+    uint64_t c[4] = {(uint64_t)(2 * j + hl), (uint64_t)qrow, (uint64_t)bh, 0ull};
+    philox4x64_10(c, p.seed, p.rng_off);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t w = (uint32_t)(c[q >> 1] >> (32 * (q & 1)));
+      dm[q] = ((w & 0xffffu) < p.keep_thr ? 0x0000ffffu : 0u) | ((w >> 16) < p.keep_thr ? 0xffff0000u : 0u);
+    }
+  }
+
+  __device__ __forceinline__ void exp_p(const f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1],
+                                        const uint32_t (&dm)[8]) {
     const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
@@ -493,6 +544,10 @@ struct FwdTile {
             g[e] = pack2<MK>(x0 - unpack_lo<MK>(f[e]), x1 - unpack_hi<MK>(f[e]));
             l_run = add_pair<MK>(g[e], l_run);
           }
+          if constexpr (DROP) {   // l keeps every P; V sees the kept ones
+            f[e] &= dm[4 * half + e];
+            if constexpr (SPLIT_P) g[e] &= dm[4 * half + e];
+          }
         }
         pf[kb * 2 + half] = f;
         if constexpr (SPLIT_P) pl[kb * 2 + half] = g;
@@ -500,10 +555,11 @@ struct FwdTile {
     }
   }
 
-  __device__ __forceinline__ void softmax(int j, f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1]) {
+  __device__ __forceinline__ void softmax(int j, f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1],
+                                          const uint32_t (&dm)[8]) {
     mask_s(j, s);
     rescale_s(s);
-    exp_p(s, pf, pl);
+    exp_p(s, pf, pl, dm);
   }
 
   // ---- O^T += V^T P^T for one tile (buffer BUF); the V fragments of step
@@ -534,8 +590,10 @@ struct FwdTile {
     f32x16 s[NKB];
     u32x4 pf[NST];
     u32x4 pl[SPLIT_P ? NST : 1];
+    uint32_t dm[8];
+    if constexpr (DROP) drop_masks(j, dm);
     gemm_s<BUF>(s);
-    softmax(j, s, pf, pl);
+    softmax(j, s, pf, pl, dm);
     gemm_pv<BUF>(pf, pl);
   }
 
@@ -591,6 +649,7 @@ struct FwdTile {
     const bool any = l_tot > 0.f;
     float inv_l = any ? 1.f / l_tot : 0.f;
     if constexpr (F8) inv_l *= *p.descale_v;
+    if constexpr (DROP) inv_l *= p.inv_keep;
     if (qrow >= Sq) return;
     char* orow = p.o + (qbase + qrow * p.q_ss) * (OUT == OF32 ? 4 : 2);
 #pragma unroll
@@ -704,6 +763,17 @@ __host__ __device__ constexpr int waves_for(int d, bool causal) { return (causal
 template <int D, bool CAUSAL, int KIND, int OUT, bool SPLIT>
 __global__ __launch_bounds__(64 * waves_for(D, CAUSAL)) __attribute__((amdgpu_waves_per_eu(3))) void fa_fwd_kernel(Params p) {
   using Blk = FwdTile<D, 32, waves_for(D, CAUSAL), FA_NBUF, CAUSAL, KIND, OUT, SPLIT>;
+  __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
+  Blk blk(p, smem);
+  blk.run();
+}
+
+// The forward with dropout: a separate instance (the keep test adds one
+// Philox call per lane and tile, so it gets the register budget of two
+// waves per SIMD).
+template <int D, bool CAUSAL, int KIND, int OUT>
+__global__ __launch_bounds__(64 * waves_for(D, CAUSAL)) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_drop_kernel(Params p) {
+  using Blk = FwdTile<D, 32, waves_for(D, CAUSAL), FA_NBUF, CAUSAL, KIND, OUT, false, true>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
@@ -844,6 +914,10 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
   p.cu_k = nullptr;
   p.br = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT;
   p.xcd_unit = 0;
+  p.seed = 0;
+  p.rng_off = 0;
+  p.keep_thr = 0;
+  p.inv_keep = 1.f;
   c.nw = nw;
   c.BH = BH;
   c.nqb = nqb;
@@ -866,6 +940,20 @@ KernelFn pick_kernel(const Call& c) {
   if (c.in_dtype == FA_BF16)
     return (c.o_dtype == FA_F32) ? pick_d<fa::KBF16, fa::OF32, false>(c.D, c.causal) : pick_d<fa::KBF16, fa::OBF16, false>(c.D, c.causal);
   return (c.o_dtype == FA_F32) ? pick_d<fa::KFP8, fa::OF32, false>(c.D, c.causal) : pick_d<fa::KFP8, fa::OF16, false>(c.D, c.causal);
+}
+
+template <int KIND, int OUT>
+KernelFn pick_drop_d(int64_t D, bool causal) {
+  if (D == 64) return causal ? fa::fa_fwd_drop_kernel<64, true, KIND, OUT> : fa::fa_fwd_drop_kernel<64, false, KIND, OUT>;
+  return causal ? fa::fa_fwd_drop_kernel<128, true, KIND, OUT> : fa::fa_fwd_drop_kernel<128, false, KIND, OUT>;
+}
+
+KernelFn pick_drop(const Call& c) {
+  if (c.in_dtype == FA_F16)
+    return (c.o_dtype == FA_F32) ? pick_drop_d<fa::KF16, fa::OF32>(c.D, c.causal) : pick_drop_d<fa::KF16, fa::OF16>(c.D, c.causal);
+  if (c.in_dtype == FA_BF16)
+    return (c.o_dtype == FA_F32) ? pick_drop_d<fa::KBF16, fa::OF32>(c.D, c.causal) : pick_drop_d<fa::KBF16, fa::OBF16>(c.D, c.causal);
+  return (c.o_dtype == FA_F32) ? pick_drop_d<fa::KFP8, fa::OF32>(c.D, c.causal) : pick_drop_d<fa::KFP8, fa::OF16>(c.D, c.causal);
 }
 
 MergeFn pick_merge(const Call& c) {
@@ -1044,6 +1132,31 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   else if ((B * H) % 8 == 0)
     p.xcd_unit = (int32_t)nqb;
   hipLaunchKernelGGL(pick_kernel<false>(c), dim3((unsigned)p.total), dim3(64 * c.nw), 0, stream, p);
+  return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
+                           fa_layout_t layout, float scale, fa_mask_t mask, float keep_prob,
+                           uint64_t seed, uint64_t offset, fa_dtype_t in_dtype,
+                           fa_dtype_t o_dtype, const float* descale_q, const float* descale_k,
+                           const float* descale_v, hipStream_t stream) {
+  if (!(keep_prob > 0.f && keep_prob <= 1.f)) return FA_ERR_UNSUPPORTED_DROPOUT;
+  Call c;
+  const fa_status_t st = check_call(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask,
+                                    1.0f, in_dtype, o_dtype, descale_q, descale_k, descale_v, c);
+  if (st != FA_OK) return st;
+  if (keep_prob == 1.f) {   // nothing is dropped
+    hipLaunchKernelGGL(pick_kernel<false>(c), dim3((unsigned)c.p.total), dim3(64 * c.nw), 0, stream, c.p);
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+  }
+  Params p = c.p;
+  long t = lrintf(keep_prob * 65536.0f);
+  p.keep_thr = (uint32_t)(t < 1 ? 1 : (t > 65535 ? 65535 : t));
+  p.inv_keep = 1.0f / keep_prob;
+  p.seed = seed;
+  p.rng_off = offset;
+  hipLaunchKernelGGL(pick_drop(c), dim3((unsigned)p.total), dim3(64 * c.nw), 0, stream, p);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -11,6 +11,7 @@ Options:
   --warmup W    untimed steps first (default 30: the clocks settle under load)
   --workload I  index into the workload list (default: the headline, 2)
   --pass P      fwd (default) or bwd
+  --keep-prob K forward with dropout (keep probability K < 1, seed 0)
   --no-cpu      skip the CPU-oracle baseline leg
   --cpu-seconds approximate CPU budget for the oracle leg (default 15)
 """
@@ -136,6 +137,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd")
+    ap.add_argument("--keep-prob", type=float, default=1.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -188,6 +190,9 @@ def main():
         if bwd:
             fa.fa_bwd(q, k, v, o, dout, lse, scale=cfg.scale, causal=cfg.causal, dq=grads[0],
                       dk=grads[1], dv=grads[2], workspace=ws)
+        elif args.keep_prob != 1.0:
+            fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse,
+                      keep_prob=args.keep_prob, seed=0, **kw)
         else:
             fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse, **kw)
 
@@ -217,7 +222,7 @@ def main():
     achieved = flops / (avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None if bwd else measured_traffic(),
+                "traffic": None if (bwd or args.keep_prob != 1.0) else measured_traffic(),
                 "kernel": "fa_bwd (row pass, dK/dV and dQ kernels; one call)" if bwd
                 else "fa_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
                 "median_launch_ms": round(med_ms, 4), "min_launch_ms": round(min(per_launch_ms), 4)}
@@ -241,11 +246,14 @@ def main():
         "config": {"workload": cfg.name, "B": cfg.B, "H": cfg.H, "Sq": cfg.Sq, "Sk": cfg.Sk,
                    "D": cfg.D, "causal": cfg.causal, "in_dtype": cfg.dtype,
                    "o_dtype": cfg.o_dtype, "layout": "BNSD", "flop_per_step": flops,
-                   "pass": args.which},
+                   "pass": args.which, "keep_prob": args.keep_prob},
         "roofline": roofline,
         "device": device_info(),
     }
-    if not args.no_cpu:
+    if args.keep_prob != 1.0:
+        out["metric"] += f", dropout keep_prob {args.keep_prob}"
+        out["roofline"]["kernel"] = "fa_fwd_drop_kernel"
+    if not args.no_cpu and args.keep_prob == 1.0:
         out["cpu_baseline"] = (cpu_baseline_bwd(cfg, inp, dout_cpu, args.cpu_seconds) if bwd
                                else cpu_baseline(cfg, inp, args.cpu_seconds))
     print(json.dumps(out), flush=True)

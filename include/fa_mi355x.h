@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 5
+#define FA_ABI_VERSION 6
 
 typedef enum {
   FA_OK = 0,
@@ -204,6 +204,29 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
                           float keep_prob, fa_dtype_t in_dtype, fa_dtype_t o_dtype,
                           const float* descale_q, const float* descale_k, const float* descale_v,
                           hipStream_t stream);
+
+/*
+ * fa_fwd_dropout — the forward of fa_fwd_ex (one key range) with dropout on
+ * the normalised probabilities: O = (P * Z / keep_prob) V, lse over all
+ * visible keys as without dropout. The pages pass keep_prob through the
+ * call ("Tracing npu_flash_attention through the CANN runtime", layer 1)
+ * without defining it; this is inverted dropout with a stated mask:
+ * Philox4x64-10 (Salmon et al., SC 2011) keyed by (seed, offset); for query
+ * head index bh = b*H + h, query row i, 32-key tile t and half u in {0, 1},
+ * the counter (2t + u, i, bh, 0) gives 256 bits read as sixteen 16-bit
+ * values (value n = bits 16n .. 16n+15, first output word lowest); key
+ * 32t + 8m + 4u + e (m, e in 0..3) takes value 4m + e and is kept iff it is
+ * below round(keep_prob * 65536) (clamped to 1..65535). The same (seed,
+ * offset) give the same mask on every call. keep_prob in (0, 1] (1: no
+ * dropout); otherwise FA_ERR_UNSUPPORTED_DROPOUT. Other arguments and errors
+ * as fa_fwd_ex.
+ */
+fa_status_t fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
+                           fa_layout_t layout, float scale, fa_mask_t mask, float keep_prob,
+                           uint64_t seed, uint64_t offset, fa_dtype_t in_dtype,
+                           fa_dtype_t o_dtype, const float* descale_q, const float* descale_k,
+                           const float* descale_v, hipStream_t stream);
 
 /*
  * Backward pass: the gradients of O = softmax(scale * Q K^T + mask) V for a

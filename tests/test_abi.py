@@ -41,7 +41,7 @@ def test_library_holds_gfx950_code():
 
 def test_abi_version_and_status_strings():
     lib = fa.load_library()
-    assert lib.fa_abi_version() == 5
+    assert lib.fa_abi_version() == 6
     names = [fa.status_str(c) for c in range(13)]
     assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP" and names[11] == "FA_ERR_WORKSPACE"
     assert names[12] == "FA_ERR_UNSUPPORTED_MASK"
@@ -274,3 +274,35 @@ def test_bwd_workspace_size():
 ])
 def test_bwd_rejects_before_launch(over, code):
     assert call_bwd(**over) == code
+
+
+# ---- dropout ----
+def call_drop(**over):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=4, H_kv=2, Sq=64, Sk=64, D=128,
+             layout=fa.FA_LAYOUT_BNSD, scale=0.125, mask=fa.FA_MASK_NONE, keep_prob=0.9,
+             seed=1, offset=0, in_dtype=fa.FA_F16, o_dtype=fa.FA_F16, descale_q=None,
+             descale_k=None, descale_v=None, stream=None)
+    a.update(over)
+    return fa.fa_fwd_dropout_raw(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(keep_prob=0.0), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(keep_prob=-0.5), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(keep_prob=1.5), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(keep_prob=float("nan")), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(H_kv=3), fa.FA_ERR_BAD_SHAPE),
+    (dict(D=80), fa.FA_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(mask=9), fa.FA_ERR_UNSUPPORTED_MASK),
+    (dict(o=K), fa.FA_ERR_ALIASING),
+])
+def test_dropout_rejects_before_launch(over, code):
+    assert call_drop(**over) == code
+
+
+def test_dropout_needs_a_seed():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        fa.fa_fwd(x, x, x, keep_prob=0.9)
