@@ -70,6 +70,16 @@ def measured_traffic():
     return d.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg, inp, budget_s: float):
     """The oracle, as it stands, on a bounded sample of whole heads."""
     import numpy as np
@@ -97,7 +107,8 @@ def cpu_baseline(cfg, inp, budget_s: float):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"{heads} of {cfg.B * cfg.H} heads of {cfg.name}, fp64 numpy, "
-                      f"{dt:.1f} s; value = algorithmic FLOP of the sample / wall time"}
+                      f"{dt:.1f} s; value = algorithmic FLOP of the sample / wall time",
+            "cpu": cpu_model()}
 
 
 def cpu_baseline_bwd(cfg, inp, dout, budget_s: float):
@@ -127,7 +138,8 @@ def cpu_baseline_bwd(cfg, inp, dout, budget_s: float):
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"backward of {heads} of {cfg.B * cfg.H} heads of {cfg.name}, fp64 numpy, "
-                      f"{dt:.1f} s; value = 2.5 x forward flop of the sample / wall time"}
+                      f"{dt:.1f} s; value = 2.5 x forward flop of the sample / wall time",
+            "cpu": cpu_model()}
 
 
 def main():
