@@ -175,9 +175,14 @@ def attention_varlen_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_
 
 
 def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
-                       scale: float, causal: bool, offset: int = 0):
+                       scale: float, causal: bool, offset: int = 0, keep_prob: float = 1.0,
+                       seed: int = 0, rng_offset: int = 0):
     """Gradients of the BNSD forward for the cotangent ``do`` [B,H,Sq,D]:
-    returns dq [B,H,Sq,D], dk, dv [B,H_kv,Sk,D]."""
+    returns dq [B,H,Sq,D], dk, dv [B,H_kv,Sk,D]. With keep_prob < 1, of the
+    forward with dropout (attention_dropout_fp64, same mask): the mask Z is
+    fixed, O = (P * Z / keep_prob) V, so dV = (P * Z / keep_prob)^T dO and
+    the gradient reaching P is dP * Z / keep_prob, which then passes the
+    softmax Jacobian as above."""
     group = _check(q, k, v)
     if do.shape != q.shape:
         raise ValueError("do must have q's shape")
@@ -185,14 +190,19 @@ def attention_bwd_fp64(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
+    Sk = k.shape[2]
     for b in range(B):
         for h in range(H):
             kv = h // group
             _, _, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal,
                                    return_p=True, offset=offset)
+            zk = 1.0
+            if keep_prob != 1.0:
+                zk = dropout_keep_mask(b * H + h, range(Sq), Sk, keep_prob, seed,
+                                       rng_offset) / keep_prob
             g = np.asarray(do[b, h], np.float64)
-            dv[b, kv] += p.T @ g                                       # dV = P^T dO
-            dp = g @ np.asarray(v[b, kv], np.float64).T                # dP = dO V^T
+            dv[b, kv] += (p * zk).T @ g                                # dV = (P Z/keep)^T dO
+            dp = (g @ np.asarray(v[b, kv], np.float64).T) * zk         # dP = dO V^T (Z/keep)
             ds = p * (dp - np.sum(p * dp, axis=1, keepdims=True))      # softmax Jacobian
             dq[b, h] = scale * (ds @ np.asarray(k[b, kv], np.float64))  # dQ = scale dS K
             dk[b, kv] += scale * (ds.T @ np.asarray(q[b, h], np.float64))   # dK = scale dS^T Q

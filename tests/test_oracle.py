@@ -946,3 +946,77 @@ def test_dropout_pins_accept_correct_copy():
     fn, mfn = _dmutant("none")
     for pin in DPINS:
         pin(fn, mfn)
+
+
+# ------------------------------------------------ backward with dropout ----
+
+def test_oracle_backward_dropout_finite_differences():
+    """With the mask fixed the dropped forward is differentiable: central
+    differences of the oracle's own dropout forward (whose mask is pinned
+    above), every element of q, k and v."""
+    h = 1e-6
+    for (H, Hkv, Sq, Sk, causal, off, keep, seed) in [(2, 1, 3, 40, True, 37, 0.6, 3),
+                                                      (2, 2, 4, 5, False, 0, 0.5, 4)]:
+        q = rand((1, H, Sq, 3), 500 + seed)
+        k = rand((1, Hkv, Sk, 3), 501 + seed)
+        v = rand((1, Hkv, Sk, 3), 502 + seed)
+        do = rand((1, H, Sq, 3), 503 + seed)
+        dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.8, causal, off, keep, seed, 9)
+
+        def loss():
+            o, _ = attention_dropout_fp64(q, k, v, 0.8, causal, off, keep, seed, 9)
+            return float(np.sum(o * do))
+        for x, g in ((q, dq), (k, dk), (v, dv)):
+            for idx in np.ndindex(x.shape):
+                keep_x = x[idx]
+                x[idx] = keep_x + h
+                lp = loss()
+                x[idx] = keep_x - h
+                lm = loss()
+                x[idx] = keep_x
+                assert abs((lp - lm) / (2 * h) - g[idx]) <= 1e-6, (idx, g[idx])
+
+
+def test_oracle_backward_dropout_torch_autograd():
+    """torch autograd (fp64) through softmax, the fixed mask and P V."""
+    H, Hkv, Sq, Sk, off, keep = 4, 2, 9, 37, 28, 0.7
+    q = rand((1, H, Sq, 8), 511)
+    k = rand((1, Hkv, Sk, 8), 512)
+    v = rand((1, Hkv, Sk, 8), 513)
+    do = rand((1, H, Sq, 8), 514)
+    dq, dk, dv = attention_bwd_fp64(q, k, v, do, 0.4, True, off, keep, 21, 2)
+    z = np.stack([dropout_keep_mask(h, range(Sq), Sk, keep, 21, 2) for h in range(H)])[None]
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    s = tq @ tk.repeat_interleave(H // Hkv, dim=1).transpose(-1, -2) * 0.4
+    vis = torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + off
+    p = torch.softmax(s.masked_fill(~vis, -math.inf), dim=-1)
+    o = (p * torch.from_numpy(z) / keep) @ tv.repeat_interleave(H // Hkv, dim=1)
+    o.backward(torch.from_numpy(do))
+    for mine, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        assert np.max(np.abs(mine - ref.numpy())) <= 1e-10
+
+
+def test_oracle_backward_keep_one_is_plain():
+    q, k, v, do = (rand((1, 2, 5, 4), 520 + i) for i in range(4))
+    a = attention_bwd_fp64(q, k, v, do, 0.5, True, 0)
+    b = attention_bwd_fp64(q, k, v, do, 0.5, True, 0, 1.0, 7, 7)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_backward_dropout_pins_catch_planted_mistakes():
+    """Mask dropped from dP, or from dV: the autograd comparison fails."""
+    H, Sq, Sk, keep = 2, 6, 40, 0.6
+    q, k, v, do = (rand((1, H, Sq if i in (0, 3) else Sk, 4), 530 + i) for i in range(4))
+    z = np.stack([dropout_keep_mask(h, range(Sq), Sk, keep, 5, 0) for h in range(H)])[None] / keep
+    tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
+    p = torch.softmax(tq @ tk.transpose(-1, -2) * 0.5, dim=-1)
+    ((p * torch.from_numpy(z)) @ tv).backward(torch.from_numpy(do))
+    pn = p.detach().numpy()
+    for kind in ("no_mask_on_dp", "no_mask_on_dv"):
+        dp = do @ v.transpose(0, 1, 3, 2) * (1.0 if kind == "no_mask_on_dp" else z)
+        ds = pn * (dp - np.sum(pn * dp, axis=-1, keepdims=True))
+        dv = (pn * (1.0 if kind == "no_mask_on_dv" else z)).transpose(0, 1, 3, 2) @ do
+        dq = 0.5 * ds @ k
+        bad = [np.max(np.abs(a - b.numpy())) > 1e-8 for a, b in ((dq, tq.grad), (dv, tv.grad))]
+        assert any(bad), kind
