@@ -35,7 +35,7 @@ FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL_TOP_LEFT, FA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
-           "fa_fwd_varlen", "fa_fwd_dropout", "fa_bwd", "fa_bwd_workspace_size", "fa_status_str",
+           "fa_fwd_varlen", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout", "fa_bwd_workspace_size", "fa_status_str",
            "fa_abi_version")
 
 _lib = None
@@ -87,6 +87,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            ctypes.c_float, ctypes.c_int,    # scale mask
                            ctypes.c_int, ctypes.c_int,      # in_dtype grad_dtype
                            vp, i64, vp]                     # workspace size stream
+    lib.fa_bwd_dropout.restype = ctypes.c_int
+    lib.fa_bwd_dropout.argtypes = lib.fa_bwd.argtypes[:17] + [ctypes.c_float, ctypes.c_uint64,
+                                                              ctypes.c_uint64] + lib.fa_bwd.argtypes[17:]
     lib.fa_bwd_workspace_size.restype = i64
     lib.fa_bwd_workspace_size.argtypes = [i64, i64, i64]
     lib.fa_fwd_splitkv_workspace_size.restype = i64
@@ -156,6 +159,15 @@ def fa_bwd_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D, scale, 
     return load_library().fa_bwd(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D,
                                  scale, mask, in_dtype, grad_dtype, workspace, workspace_size,
                                  stream)
+
+
+def fa_bwd_dropout_raw(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D, scale, mask,
+                       keep_prob, seed, offset, in_dtype, grad_dtype, workspace, workspace_size,
+                       stream) -> int:
+    """The backward-with-dropout C entry point with integer pointers."""
+    return load_library().fa_bwd_dropout(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk,
+                                         D, scale, mask, keep_prob, seed, offset, in_dtype,
+                                         grad_dtype, workspace, workspace_size, stream)
 
 
 def bwd_workspace_size(B, H, Sq) -> int:
@@ -293,7 +305,8 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
 
 
 def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = False,
-           grad_dtype=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+           grad_dtype=None, dq=None, dk=None, dv=None, workspace=None, stream=None,
+           keep_prob: float = 1.0, seed: int | None = None, rng_offset: int = 0):
     """Gradients (dq, dk, dv) of the attention forward for the cotangent
     ``dout``, from the forward's output ``o`` and ``lse``.
 
@@ -302,6 +315,8 @@ def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = 
     ``grad_dtype``: dtype of the gradients (default: the input dtype; or
     float32). ``workspace``: an optional uint8 GPU tensor of at least
     ``bwd_workspace_size(B, H, Sq)`` bytes (allocated here when not given).
+    ``keep_prob`` < 1: the backward of fa_fwd with dropout; ``seed`` and
+    ``rng_offset`` must be the forward's.
     """
     import torch
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
@@ -342,10 +357,18 @@ def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = 
     ws_size = workspace.numel() - (ws - base)
     if stream is None:
         stream = torch.cuda.current_stream(dev).cuda_stream
-    _check_status(fa_bwd_raw(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, Hkv, Sq, Sk, D, float(scale),
-        _mask_code(causal), _dtype_code(q.dtype), _dtype_code(dq.dtype), ws, ws_size, stream))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr())
+    shape = (B, H, Hkv, Sq, Sk, D, float(scale), _mask_code(causal))
+    tail = (_dtype_code(q.dtype), _dtype_code(dq.dtype), ws, ws_size, stream)
+    if keep_prob != 1.0:
+        if seed is None:
+            raise ValueError("dropout (keep_prob < 1) needs the forward's seed")
+        _check_status(fa_bwd_dropout_raw(*ptrs, *shape, float(keep_prob),
+                                         int(seed) & ((1 << 64) - 1),
+                                         int(rng_offset) & ((1 << 64) - 1), *tail))
+    else:
+        _check_status(fa_bwd_raw(*ptrs, *shape, *tail))
     return dq, dk, dv
 
 

@@ -31,6 +31,15 @@
 //  * dq: the forward's structure, one workgroup per 128 query rows, K and V
 //    tiles (32 keys) streamed through LDS: S^T = K Q^T, dP^T = V dO^T, then
 //    dQ^T += K^T dS^T with K^T read transposed.
+//
+// Dropout (DROP): the forward's mask Z (Philox4x64-10, counter (2t + half,
+// query row, b*H + h, 0) per 16 keys of a 32-key tile t) is drawn again;
+// P * Z / keep_prob multiplies dO in dV, and dP * Z / keep_prob is the
+// gradient reaching P. The dq kernel holds the forward's layout (a lane owns
+// one query row and the 16 keys of one Philox block per tile). In the dkv
+// kernel a lane owns one key and 16 query rows, so each lane draws the block
+// of one (row, half) of its wave's tile, reduces it to 16 keep bits and the
+// lanes exchange the bits through 128 bytes of LDS per wave.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -62,6 +71,9 @@ struct BwdParams {
   int32_t total;        // workgroups of the launch
   float scale;          // S = scale * Q K^T
   float c;              // scale * log2(e)
+  uint64_t seed, rng_off;   // dropout: Philox key
+  uint32_t keep_thr;        // a 16-bit draw below this keeps its P
+  float inv_keep;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -188,8 +200,19 @@ __device__ __forceinline__ void store4(char* row, int d, float a, float b, float
   }
 }
 
+// 16 keep bits of one Philox block: bit n set iff 16-bit value n of the
+// output lies below the threshold
+__device__ __forceinline__ uint32_t keep_bits16(uint64_t c0, uint64_t c1, uint64_t c2, const BwdParams& p) {
+  uint64_t c[4] = {c0, c1, c2, 0ull};
+  philox4x64_10(c, p.seed, p.rng_off);
+  uint32_t m = 0;
+#pragma unroll
+  for (int n = 0; n < 16; ++n) m |= ((uint32_t)(c[n >> 2] >> (16 * (n & 3))) & 0xffffu) < p.keep_thr ? (1u << n) : 0u;
+  return m;
+}
+
 // ============================== dK, dV ==============================
-template <int D, bool CAUSAL, int KIND, int OUT>
+template <int D, bool CAUSAL, int KIND, int OUT, bool DROP>
 struct BwdDkv {
   static constexpr int NW = 4;                // waves, 32 keys each
   static constexpr int BK = 32 * NW;          // keys per workgroup
@@ -201,7 +224,8 @@ struct BwdDkv {
   static constexpr int BUF = 2 * TQ + 256;    // Q, dO, lse2[32], Delta[32]
   static constexpr int VOFF = 0;              // V block (BK rows)
   static constexpr int ROFF = BK * RB;        // ring of two tile buffers
-  static constexpr int SMEM = ROFF + 2 * BUF;
+  static constexpr int ZOFF = ROFF + 2 * BUF; // dropout: keep bits, 32 rows x 4 bytes per wave
+  static constexpr int SMEM = ZOFF + (DROP ? NW * 128 : 0);
 
   const BwdParams& p;
   uint32_t lds0;
@@ -299,6 +323,25 @@ struct BwdDkv {
     const uint32_t ob = qb + TQ;
     const uint32_t lb = qb + 2 * TQ;
     const uint32_t vb = lds0 + VOFF + 32 * wave * RB;
+    uint32_t zbits = 0;   // dropout: bit r = keep bit of this lane's key in row r
+    if constexpr (DROP) {
+      // this lane draws row q0 + l32, half hl of the wave's 32-key tile and
+      // stores its 16 keep bits; the word of row r holds half 0 in bits
+      // 0..15 and half 1 in bits 16..31
+      const int64_t bhq = (int64_t)b * p.H + (int64_t)kvh * group + hh;
+      const uint32_t m = keep_bits16((uint64_t)(2 * (kw0 / 32) + hl), (uint64_t)(q0 + l32), (uint64_t)bhq, p);
+      const uint32_t zb = lds0 + ZOFF + wave * 128;
+      *LDS_PTR(uint16_t, zb + l32 * 4 + hl * 2) = (uint16_t)m;
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // key offset l32 of the tile: half (l32/4)&1, value 4*(l32/8) + l32%4
+      const int bit = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 w = lds_load<u32x4>(zb + (8 * g + 4 * hl) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) zbits |= ((w[e] >> bit) & 1u) << (4 * g + e);
+      }
+    }
 
     // S = Q K^T, dP = dO V^T: lane = key (l32), rows = queries
     f32x16 s = (f32x16){}, dp = (f32x16){};
@@ -328,8 +371,14 @@ struct BwdDkv {
         float x = __builtin_fmaf(s[r], p.c, -l2[e]);
         if (CAUSAL && need_mask && (8 * g + e) < lim) x = -INFINITY;
         const float pr = __builtin_amdgcn_exp2f(x);
-        s[r] = pr;
-        dp[r] = pr * (dp[r] - dl[e]);
+        if constexpr (DROP) {
+          const float z = ((zbits >> r) & 1u) ? p.inv_keep : 0.f;
+          s[r] = pr * z;
+          dp[r] = pr * (dp[r] * z - dl[e]);
+        } else {
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - dl[e]);
+        }
       }
     }
     u32x4 pf[2], dsf[2];
@@ -373,7 +422,7 @@ struct BwdDkv {
 };
 
 // ================================ dQ ================================
-template <int D, bool CAUSAL, int KIND, int OUT>
+template <int D, bool CAUSAL, int KIND, int OUT, bool DROP>
 struct BwdDq {
   static constexpr int NW = 4;                // waves, 32 query rows each
   static constexpr int BM = 32 * NW;
@@ -465,6 +514,8 @@ struct BwdDq {
     const uint32_t kb = lds0 + buf * BUF;
     const uint32_t vb = kb + TILE;
     const int64_t kt0 = (int64_t)j * BN;
+    uint32_t zm = 0;
+    if constexpr (DROP) zm = keep_bits16((uint64_t)(2 * j + hl), (uint64_t)qrow, (uint64_t)bh, p);
     // S^T = K Q^T, dP^T = V dO^T: lane = query (l32), rows = keys
     f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
@@ -490,7 +541,13 @@ struct BwdDq {
       float x = __builtin_fmaf(s[r], p.c, -l2);
       if (need_mask && (8 * (r >> 2) + (r & 3)) >= lim) x = -INFINITY;
       const float pr = __builtin_amdgcn_exp2f(x);
-      dp[r] = pr * (dp[r] - dl);
+      if constexpr (DROP) {
+        // register r holds Philox value r of this lane's block
+        const float z = ((zm >> r) & 1u) ? p.inv_keep : 0.f;
+        dp[r] = pr * (dp[r] * z - dl);
+      } else {
+        dp[r] = pr * (dp[r] - dl);
+      }
     }
     // dQ^T += K^T dS^T
 #pragma unroll
@@ -521,17 +578,17 @@ struct BwdDq {
   }
 };
 
-template <int D, bool CAUSAL, int KIND, int OUT>
+template <int D, bool CAUSAL, int KIND, int OUT, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dkv_kernel(BwdParams p) {
-  using Blk = BwdDkv<D, CAUSAL, KIND, OUT>;
+  using Blk = BwdDkv<D, CAUSAL, KIND, OUT, DROP>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
 }
 
-template <int D, bool CAUSAL, int KIND, int OUT>
+template <int D, bool CAUSAL, int KIND, int OUT, bool DROP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(BwdParams p) {
-  using Blk = BwdDq<D, CAUSAL, KIND, OUT>;
+  using Blk = BwdDq<D, CAUSAL, KIND, OUT, DROP>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
@@ -548,21 +605,21 @@ typedef void (*BwdFn)(BwdParams);
 typedef void (*PreFn)(BwdParams, int64_t);
 
 template <int D, bool CAUSAL, int KIND, int OUT>
-void pick_pair(BwdFn& dkv, BwdFn& dq) {
-  dkv = fa::fa_bwd_dkv_kernel<D, CAUSAL, KIND, OUT>;
-  dq = fa::fa_bwd_dq_kernel<D, CAUSAL, KIND, OUT>;
+void pick_pair(bool drop, BwdFn& dkv, BwdFn& dq) {
+  dkv = drop ? fa::fa_bwd_dkv_kernel<D, CAUSAL, KIND, OUT, true> : fa::fa_bwd_dkv_kernel<D, CAUSAL, KIND, OUT, false>;
+  dq = drop ? fa::fa_bwd_dq_kernel<D, CAUSAL, KIND, OUT, true> : fa::fa_bwd_dq_kernel<D, CAUSAL, KIND, OUT, false>;
 }
 
 template <int D, int KIND, int OUT>
-void pick_c(bool causal, BwdFn& dkv, BwdFn& dq) {
-  if (causal) pick_pair<D, true, KIND, OUT>(dkv, dq);
-  else pick_pair<D, false, KIND, OUT>(dkv, dq);
+void pick_c(bool causal, bool drop, BwdFn& dkv, BwdFn& dq) {
+  if (causal) pick_pair<D, true, KIND, OUT>(drop, dkv, dq);
+  else pick_pair<D, false, KIND, OUT>(drop, dkv, dq);
 }
 
 template <int D, int KIND>
-void pick_o(bool f32, bool causal, BwdFn& dkv, BwdFn& dq) {
-  if (f32) pick_c<D, KIND, fa::OF32>(causal, dkv, dq);
-  else pick_c<D, KIND, KIND == fa::KBF16 ? fa::OBF16 : fa::OF16>(causal, dkv, dq);
+void pick_o(bool f32, bool causal, bool drop, BwdFn& dkv, BwdFn& dq) {
+  if (f32) pick_c<D, KIND, fa::OF32>(causal, drop, dkv, dq);
+  else pick_c<D, KIND, KIND == fa::KBF16 ? fa::OBF16 : fa::OF16>(causal, drop, dkv, dq);
 }
 
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -575,6 +632,13 @@ constexpr int64_t kMaxDim = int64_t(1) << 40;
 int64_t bwd_rows(int64_t B, int64_t H, int64_t Sq) { return B * H * ((Sq + 31) / 32 * 32); }
 
 }  // namespace
+
+static fa_status_t bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                       int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D, float scale, fa_mask_t mask,
+                       float keep_prob, uint64_t seed, uint64_t rng_off, fa_dtype_t in_dtype,
+                       fa_dtype_t grad_dtype, void* workspace, int64_t workspace_size,
+                       hipStream_t stream);
 
 extern "C" {
 
@@ -592,6 +656,29 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D, float scale, fa_mask_t mask,
                    fa_dtype_t in_dtype, fa_dtype_t grad_dtype, void* workspace,
                    int64_t workspace_size, hipStream_t stream) {
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D, scale, mask, 1.0f, 0, 0,
+                    in_dtype, grad_dtype, workspace, workspace_size, stream);
+}
+
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
+                           float scale, fa_mask_t mask, float keep_prob, uint64_t seed,
+                           uint64_t offset, fa_dtype_t in_dtype, fa_dtype_t grad_dtype,
+                           void* workspace, int64_t workspace_size, hipStream_t stream) {
+  if (!(keep_prob > 0.f && keep_prob <= 1.f)) return FA_ERR_UNSUPPORTED_DROPOUT;
+  return bwd_launch(q, k, v, o, dout, lse, dq, dk, dv, B, H, H_kv, Sq, Sk, D, scale, mask, keep_prob,
+                    seed, offset, in_dtype, grad_dtype, workspace, workspace_size, stream);
+}
+
+}  // extern "C"
+
+static fa_status_t bwd_launch(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                       const float* lse, void* dq, void* dk, void* dv, int64_t B, int64_t H,
+                       int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D, float scale, fa_mask_t mask,
+                       float keep_prob, uint64_t seed, uint64_t rng_off, fa_dtype_t in_dtype,
+                       fa_dtype_t grad_dtype, void* workspace, int64_t workspace_size,
+                       hipStream_t stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
   if (B < 1 || H < 1 || H_kv < 1 || Sq < 1 || Sk < 1) return FA_ERR_BAD_SHAPE;
   if (B > kMaxDim || H > kMaxDim || Sq > kMaxDim || Sk > kMaxDim) return FA_ERR_BAD_SHAPE;
@@ -652,17 +739,27 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   p.Hkv = (int32_t)H_kv;
   p.scale = scale;
   p.c = scale * fa::kLog2e;
+  const bool drop = keep_prob != 1.0f;
+  p.seed = seed;
+  p.rng_off = rng_off;
+  p.keep_thr = 0;
+  p.inv_keep = 1.f;
+  if (drop) {
+    const long t = lrintf(keep_prob * 65536.0f);
+    p.keep_thr = (uint32_t)(t < 1 ? 1 : (t > 65535 ? 65535 : t));
+    p.inv_keep = 1.0f / keep_prob;
+  }
   const bool causal = mask != FA_MASK_NONE;
   const bool f32 = grad_dtype == FA_F32;
 
   PreFn pre;
   BwdFn dkv, dq_fn;
   if (D == 64) {
-    if (in_dtype == FA_BF16) { pre = fa::fa_bwd_pre_kernel<64, fa::KBF16>; pick_o<64, fa::KBF16>(f32, causal, dkv, dq_fn); }
-    else { pre = fa::fa_bwd_pre_kernel<64, fa::KF16>; pick_o<64, fa::KF16>(f32, causal, dkv, dq_fn); }
+    if (in_dtype == FA_BF16) { pre = fa::fa_bwd_pre_kernel<64, fa::KBF16>; pick_o<64, fa::KBF16>(f32, causal, drop, dkv, dq_fn); }
+    else { pre = fa::fa_bwd_pre_kernel<64, fa::KF16>; pick_o<64, fa::KF16>(f32, causal, drop, dkv, dq_fn); }
   } else {
-    if (in_dtype == FA_BF16) { pre = fa::fa_bwd_pre_kernel<128, fa::KBF16>; pick_o<128, fa::KBF16>(f32, causal, dkv, dq_fn); }
-    else { pre = fa::fa_bwd_pre_kernel<128, fa::KF16>; pick_o<128, fa::KF16>(f32, causal, dkv, dq_fn); }
+    if (in_dtype == FA_BF16) { pre = fa::fa_bwd_pre_kernel<128, fa::KBF16>; pick_o<128, fa::KBF16>(f32, causal, drop, dkv, dq_fn); }
+    else { pre = fa::fa_bwd_pre_kernel<128, fa::KF16>; pick_o<128, fa::KF16>(f32, causal, drop, dkv, dq_fn); }
   }
   const int rpb = 256 / (int)(D / 8);
   hipLaunchKernelGGL(pre, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, p, rows);
@@ -678,5 +775,3 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   hipLaunchKernelGGL(dq_fn, dim3((unsigned)pq.total), dim3(256), 0, stream, pq);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
-
-}  // extern "C"

@@ -91,30 +91,6 @@ struct Params {
 };
 
 
-// Philox4x64-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
-// as easy as 1, 2, 3", SC 2011): ten rounds, each taking the two 128-bit
-// products of counter words 0 and 2 with the round multipliers and mixing
-// their halves with words 1 and 3 and the key; the key advances by the two
-// Weyl constants between rounds. c is the counter on entry, the output on
-// return.
-__device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
-  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += W0;
-      k1 += W1;
-    }
-    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
-    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
-    c[0] = hi1 ^ c[1] ^ k0;
-    c[1] = lo1;
-    c[2] = hi0 ^ c[3] ^ k1;
-    c[3] = lo0;
-  }
-}
-
 // One workgroup: NW waves, BM = 32 * NW query rows, 32 per wave.
 // Keys and values stream through LDS in tiles of BN rows, in a ring of NB
 // buffers per tensor: the loads of tile j+NB-1 are issued right after the

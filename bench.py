@@ -11,7 +11,8 @@ Options:
   --warmup W    untimed steps first (default 30: the clocks settle under load)
   --workload I  index into the workload list (default: the headline, 2)
   --pass P      fwd (default) or bwd
-  --keep-prob K forward with dropout (keep probability K < 1, seed 0)
+  --keep-prob K with dropout (keep probability K < 1, seed 0), forward or
+                backward
   --no-cpu      skip the CPU-oracle baseline leg
   --cpu-seconds approximate CPU budget for the oracle leg (default 15)
 """
@@ -193,7 +194,8 @@ def main():
             sys.exit(2)
         dout_cpu = fi.make_cotangent(tuple(q.shape), cfg.dtype, cfg.seed + 5000)
         dout = dout_cpu.to(dev)
-        fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse)
+        dkw = {} if args.keep_prob == 1.0 else dict(keep_prob=args.keep_prob, seed=0)
+        fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse, **dkw)
         grads = tuple(torch.empty_like(t) for t in (q, k, v))
         ws = torch.empty(fa.bwd_workspace_size(cfg.B, cfg.H, cfg.Sq) + 256, dtype=torch.uint8,
                          device=dev)
@@ -201,7 +203,7 @@ def main():
     def step():
         if bwd:
             fa.fa_bwd(q, k, v, o, dout, lse, scale=cfg.scale, causal=cfg.causal, dq=grads[0],
-                      dk=grads[1], dv=grads[2], workspace=ws)
+                      dk=grads[1], dv=grads[2], workspace=ws, **dkw)
         elif args.keep_prob != 1.0:
             fa.fa_fwd(q, k, v, scale=cfg.scale, causal=cfg.causal, out=o, lse=lse,
                       keep_prob=args.keep_prob, seed=0, **kw)
@@ -264,7 +266,8 @@ def main():
     }
     if args.keep_prob != 1.0:
         out["metric"] += f", dropout keep_prob {args.keep_prob}"
-        out["roofline"]["kernel"] = "fa_fwd_drop_kernel"
+        if not bwd:
+            out["roofline"]["kernel"] = "fa_fwd_drop_kernel"
     if not args.no_cpu and args.keep_prob == 1.0:
         out["cpu_baseline"] = (cpu_baseline_bwd(cfg, inp, dout_cpu, args.cpu_seconds) if bwd
                                else cpu_baseline(cfg, inp, args.cpu_seconds))

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 6
+#define FA_ABI_VERSION 7
 
 typedef enum {
   FA_OK = 0,
@@ -256,6 +256,22 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D, float scale, fa_mask_t mask,
                    fa_dtype_t in_dtype, fa_dtype_t grad_dtype, void* workspace,
                    int64_t workspace_size, hipStream_t stream);
+
+/*
+ * fa_bwd_dropout — the backward of fa_fwd_dropout: the same arguments as
+ * fa_bwd plus keep_prob, seed and offset, which must be those of the
+ * forward call (the mask is drawn again from them, as fa_fwd_dropout
+ * states it). o is the dropped forward output. With the mask Z fixed,
+ * dV = (P * Z / keep_prob)^T dO and dP * Z / keep_prob is the gradient
+ * reaching P (the derivative of the dropped forward). keep_prob in (0, 1]
+ * (1: fa_bwd); otherwise FA_ERR_UNSUPPORTED_DROPOUT.
+ */
+fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
+                           float scale, fa_mask_t mask, float keep_prob, uint64_t seed,
+                           uint64_t offset, fa_dtype_t in_dtype, fa_dtype_t grad_dtype,
+                           void* workspace, int64_t workspace_size, hipStream_t stream);
 
 /* Workspace bytes fa_bwd needs (8 bytes per query row, rows rounded up to a
  * multiple of 32 per head); -1 for sizes it rejects. */

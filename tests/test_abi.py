@@ -41,7 +41,7 @@ def test_library_holds_gfx950_code():
 
 def test_abi_version_and_status_strings():
     lib = fa.load_library()
-    assert lib.fa_abi_version() == 6
+    assert lib.fa_abi_version() == 7
     names = [fa.status_str(c) for c in range(13)]
     assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP" and names[11] == "FA_ERR_WORKSPACE"
     assert names[12] == "FA_ERR_UNSUPPORTED_MASK"
@@ -306,3 +306,25 @@ def test_dropout_needs_a_seed():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(ValueError):
         fa.fa_fwd(x, x, x, keep_prob=0.9)
+
+
+
+def call_bwd_drop(**over):
+    a = dict(q=Q, k=K, v=V, o=O, dout=DO, lse=L, dq=GQ, dk=GK, dv=GV, B=1, H=4, H_kv=2, Sq=100,
+             Sk=300, D=128, scale=0.125, mask=fa.FA_MASK_NONE, keep_prob=0.8, seed=3, offset=1,
+             in_dtype=fa.FA_BF16, grad_dtype=fa.FA_F32, workspace=WS, workspace_size=1 << 20,
+             stream=None)
+    a.update(over)
+    return fa.fa_bwd_dropout_raw(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(keep_prob=0.0), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(keep_prob=2.0), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(keep_prob=float("nan")), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(workspace=None), fa.FA_ERR_WORKSPACE),
+    (dict(dk=GQ), fa.FA_ERR_ALIASING),
+])
+def test_bwd_dropout_rejects_before_launch(over, code):
+    assert call_bwd_drop(**over) == code

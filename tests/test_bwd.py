@@ -23,7 +23,8 @@ import torch
 
 import attention_fa_fwd_07_amd as fa
 import fa_inputs as fi
-from oracle import attention_bwd_fp64, attention_fp64, head_forward
+from oracle import (attention_bwd_fp64, attention_dropout_fp64, attention_fp64,
+                    dropout_keep_mask, head_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -40,8 +41,9 @@ def case_inputs(dtype, B, H, Hkv, Sq, Sk, D, seed, amp=1.0):
     return cfg, inp, do
 
 
-def term_bounds(q, k, v, g, scale, causal, off):
-    """Largest sum of absolute term values per gradient tensor."""
+def term_bounds(q, k, v, g, scale, causal, off, drop=None):
+    """Largest sum of absolute term values per gradient tensor (drop: keep,
+    seed, offset of a dropout mask, whose Z / keep scales P in dV and dP)."""
     B, H, Sq, D = q.shape
     Hkv = k.shape[1]
     bq = 0.0
@@ -52,11 +54,14 @@ def term_bounds(q, k, v, g, scale, causal, off):
             kv = h // (H // Hkv)
             _, _, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal, return_p=True,
                                    offset=off)
-            dp = g[b, h] @ v[b, kv].T
+            z = 1.0
+            if drop is not None:
+                z = dropout_keep_mask(b * H + h, range(Sq), k.shape[2], *drop) / drop[0]
+            dp = (g[b, h] @ v[b, kv].T) * z
             w = p * (np.abs(dp) + np.abs(np.sum(p * dp, axis=1, keepdims=True)))
             bq = max(bq, float(np.max(abs(scale) * w @ np.abs(k[b, kv]))))
             bk[b, kv] += abs(scale) * w.T @ np.abs(q[b, h])
-            bv[b, kv] += p.T @ np.abs(g[b, h])
+            bv[b, kv] += (p * z).T @ np.abs(g[b, h])
     return bq, float(bk.max()), float(bv.max())
 
 
@@ -69,7 +74,7 @@ def oracle_all(cfg, inp, do, causal, off):
     return o, lse, (dq, dk, dv), bounds
 
 
-def run_bwd(cfg, inp, do, o, lse, causal, grad_dtype):
+def run_bwd(cfg, inp, do, o, lse, causal, grad_dtype, drop=None):
     td = fi.TORCH_DTYPE[cfg.dtype]
     q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
     ot = torch.from_numpy(o).to(torch.float32).to(td).cuda()
@@ -80,8 +85,9 @@ def run_bwd(cfg, inp, do, o, lse, causal, grad_dtype):
     dv = torch.full(tuple(v.shape), float("nan"), dtype=gd, device="cuda")
     ws = torch.full((fa.bwd_workspace_size(cfg.B, cfg.H, cfg.Sq) + 256,), 255, dtype=torch.uint8,
                     device="cuda")
+    kw = {} if drop is None else dict(keep_prob=drop[0], seed=drop[1], rng_offset=drop[2])
     fa.fa_bwd(q, k, v, ot, do.cuda(), lt, scale=cfg.scale, causal=causal, dq=dq, dk=dk, dv=dv,
-              workspace=ws)
+              workspace=ws, **kw)
     torch.cuda.synchronize()
     return tuple(t.double().cpu().numpy() for t in (dq, dk, dv))
 
@@ -167,3 +173,45 @@ def test_bwd_large_logits():
     got = run_bwd(cfg, inp, do, o, lse, True, fi.F32)
     e = check(fi.F16, got, ref, bnd, "large logits")
     print(f"large logits: rel err dq/dk/dv {e}")
+
+
+@pytest.mark.parametrize("dtype", [fi.F16, fi.BF16])
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_bwd_dropout(dtype, D, mask):
+    """The backward of the dropout forward: O and lse from the oracle's
+    dropout forward, gradients against the oracle's (same mask)."""
+    worst = [0.0, 0.0, 0.0]
+    for i, (Sq, Sk, keep) in enumerate([(1, 1, 0.9), (65, 130, 0.5), (130, 65, 0.7),
+                                        (200, 200, 0.8)]):
+        H, Hkv = ((2, 2), (4, 2), (3, 1), (2, 1))[i]
+        causal = MASKS[mask][0]
+        off = (Sk - Sq) if mask == "bottom_right" else 0
+        cfg, inp, do = case_inputs(dtype, 1, H, Hkv, Sq, Sk, D, seed=1700 + 13 * i + D)
+        drop = (keep, 77 + i, 5 * i)
+        q, k, v = fi.values(inp)
+        g = do.double().numpy()
+        o, lse = attention_dropout_fp64(q, k, v, cfg.scale, causal, off, *drop)
+        ref = attention_bwd_fp64(q, k, v, g, cfg.scale, causal, off, *drop)
+        bnd = term_bounds(q, k, v, g, cfg.scale, causal, off, drop)
+        got = run_bwd(cfg, inp, do, o, lse, False if mask == "none" else mask, fi.F32, drop)
+        e = check(dtype, got, ref, bnd, f"dropout {dtype} D{D} {mask} {Sq}x{Sk} keep {keep}")
+        worst = [max(a, b) for a, b in zip(worst, e)]
+    print(f"dropout bwd {dtype} D{D} {mask}: worst rel err dq/dk/dv {worst}")
+
+
+def test_bwd_dropout_chained_with_library_forward():
+    """fa_fwd with dropout, then fa_bwd with the same seed and offset."""
+    cfg, inp, do = case_inputs(fi.F16, 2, 4, 2, 300, 333, 128, seed=1750)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    o, lse = fa.fa_fwd(q, k, v, scale=cfg.scale, causal="bottom_right", keep_prob=0.75,
+                       seed=99, rng_offset=4)
+    dq, dk, dv = fa.fa_bwd(q, k, v, o, do.cuda(), lse, scale=cfg.scale, causal="bottom_right",
+                           grad_dtype=torch.float32, keep_prob=0.75, seed=99, rng_offset=4)
+    torch.cuda.synchronize()
+    qq, kk, vv = fi.values(inp)
+    g = do.double().numpy()
+    ref = attention_bwd_fp64(qq, kk, vv, g, cfg.scale, True, 33, 0.75, 99, 4)
+    bnd = term_bounds(qq, kk, vv, g, cfg.scale, True, 33, (0.75, 99, 4))
+    check(fi.F16, tuple(t.double().cpu().numpy() for t in (dq, dk, dv)), ref, bnd,
+          "dropout chained")
