@@ -115,3 +115,66 @@ def test_large_logits_stay_finite():
     o, lse = run_gpu(cfg, inp, fi.F32)
     compare(cfg, fi.F32, o, lse, ref_o, ref_l, what="large logits")
     assert ref_l.max() > 100
+
+
+def test_backward_offsets_past_4gib_and_side_stream():
+    """Every backward tensor and the workspace start beyond 4 GiB inside one
+    5 GiB allocation, launched on a non-default stream."""
+    from oracle import attention_bwd_fp64
+    cfg = fi.Config("far_bwd", 1, 4, 150, 170, 128, fi.F16, True, seed=82)
+    inp = fi.make_inputs(cfg)
+    inp.k = inp.k[:, :2].contiguous()
+    inp.v = inp.v[:, :2].contiguous()
+    do = fi.make_cotangent((1, 4, 150, 128), fi.F16, 83)
+    qq, kk, vv = fi.values(inp)
+    ref = attention_bwd_fp64(qq, kk, vv, do.double().numpy(), cfg.scale, True)
+    big = torch.empty(5 << 30, dtype=torch.uint8, device="cuda")
+    off = [(4 << 30) + 4096]
+
+    def place(shape, dtype):
+        n = int(np.prod(shape)) * torch.tensor([], dtype=dtype).element_size()
+        t = big[off[0]:off[0] + n].view(dtype).view(shape)
+        off[0] += ((n + 4095) // 4096) * 4096
+        return t
+
+    q = place(tuple(inp.q.shape), torch.float16)
+    k = place(tuple(inp.k.shape), torch.float16)
+    v = place(tuple(inp.v.shape), torch.float16)
+    o = place(tuple(inp.q.shape), torch.float16)
+    dout = place(tuple(inp.q.shape), torch.float16)
+    lse = place((1, 4, 150), torch.float32)
+    dq = place(tuple(inp.q.shape), torch.float32)
+    dk = place(tuple(inp.k.shape), torch.float32)
+    dv = place(tuple(inp.v.shape), torch.float32)
+    ws = place((fa.bwd_workspace_size(1, 4, 150),), torch.uint8)
+    assert q.data_ptr() - big.data_ptr() > (4 << 30)
+    q.copy_(inp.q.cuda()); k.copy_(inp.k.cuda()); v.copy_(inp.v.cuda()); dout.copy_(do.cuda())
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        fa.fa_fwd(q, k, v, scale=cfg.scale, causal=True, out=o, lse=lse)
+        fa.fa_bwd(q, k, v, o, dout, lse, scale=cfg.scale, causal=True, dq=dq, dk=dk, dv=dv,
+                  workspace=ws)
+    s.synchronize()
+    for name, g, r in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
+        e = np.abs(g.double().cpu().numpy() - r).max() / np.abs(r).max()
+        assert e <= 2 * 2.0 ** -11, (name, e)
+    del big
+
+
+def test_varlen_on_side_stream():
+    from oracle import attention_varlen_fp64
+    vi = fi.make_varlen_inputs([70, 1, 130], [90, 40, 130], 4, 2, 64, fi.F16, seed=84)
+    q, k, v = (t.cuda() for t in (vi.inp.q, vi.inp.k, vi.inp.v))
+    cq, ck = vi.cu_q.cuda(), vi.cu_k.cuda()
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        o, lse = fa.fa_fwd_varlen(q, k, v, cq, ck, vi.max_q, causal="bottom_right",
+                                  o_dtype=torch.float32)
+    s.synchronize()
+    q64, k64, v64 = fi.values(vi.inp)
+    ro, rl = attention_varlen_fp64(q64, k64, v64, vi.cu_q.numpy(), vi.cu_k.numpy(), 0.125, True,
+                                   True)
+    assert np.abs(o.double().cpu().numpy() - ro).max() <= 2e-3
+    assert np.abs(lse.double().cpu().numpy() - rl).max() <= 1e-3
