@@ -735,15 +735,16 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
 // as many K/V tiles loaded per query row, and four waves per SIMD still fit
 // the register budget at that head dim).
 __host__ __device__ constexpr int waves_for(int d, bool causal) { return (causal && d == 64) ? 8 : 4; }
-// Keys per tile: 64 for fp8 inputs (a tile is half the bytes, so the ring of
-// three still leaves room for three workgroups per CU; measured 7.5 % faster
-// on B1 H32 S8192 D128 fp8 causal), 32 otherwise (64 would leave one
-// workgroup per CU for 16-bit inputs).
-__host__ __device__ constexpr int keys_for(int kind) { return kind == KFP8 ? 64 : 32; }
+// Keys per tile: 64 where a K/V row is 128 bytes (fp8 at D=128, anything at
+// D=64: the ring of three still leaves room for three workgroups per CU;
+// measured 7.5 % faster on B1 H32 S8192 D128 fp8 causal, 8.5 % on B3 H12
+// S4097 D64 causal, 17 % on B1 H8 S512 D64), 32 for 16-bit data at D=128
+// (64 would leave one workgroup per CU).
+__host__ __device__ constexpr int keys_for(int kind, int d) { return (kind == KFP8 || d == 64) ? 64 : 32; }
 
 template <int D, bool CAUSAL, int KIND, int OUT, bool SPLIT>
 __global__ __launch_bounds__(64 * waves_for(D, CAUSAL)) __attribute__((amdgpu_waves_per_eu(3))) void fa_fwd_kernel(Params p) {
-  using Blk = FwdTile<D, keys_for(KIND), waves_for(D, CAUSAL), FA_NBUF, CAUSAL, KIND, OUT, SPLIT>;
+  using Blk = FwdTile<D, keys_for(KIND, D), waves_for(D, CAUSAL), FA_NBUF, CAUSAL, KIND, OUT, SPLIT>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);
   blk.run();
