@@ -44,6 +44,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <float.h>
 
 #include "fa_mi355x.h"
 #include "fa_device.h"
@@ -69,8 +70,9 @@ struct BwdParams {
   int32_t H, Hkv;
   int32_t nblk;         // blocks per head (dq) or per key/value head (dkv)
   int32_t total;        // workgroups of the launch
-  float scale;          // S = scale * Q K^T
-  float c;              // scale * log2(e)
+  float scale;          // S = scale * Q K^T (dQ and dK carry it with its sign)
+  float c;              // max(|scale| * log2(e), FLT_MIN)
+  int32_t negate;       // scale < 0: the register operand of S is negated (exact)
   uint64_t seed, rng_off;   // dropout: Philox key
   uint32_t keep_thr;        // a 16-bit draw below this keeps its P
   float inv_keep;
@@ -299,7 +301,10 @@ struct BwdDkv {
       const int64_t key = kw0 + l32 < p.Sk ? kw0 + l32 : p.Sk - 1;
       const char* kr = kvbase(p.k, p.k_ss) + key * p.k_ss * 2;
 #pragma unroll
-      for (int ds = 0; ds < NDS; ++ds) kf[ds] = *(const u32x4*)(kr + (16 * ds + 8 * hl) * 2);
+      for (int ds = 0; ds < NDS; ++ds) {
+        kf[ds] = *(const u32x4*)(kr + (16 * ds + 8 * hl) * 2);
+        if (p.negate) kf[ds] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      }
     }
     for (int it = 0; it < ntot; ++it) {
       wait_loads<0>();
@@ -483,6 +488,7 @@ struct BwdDq {
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) {
       qf[ds] = *(const u32x4*)(qp + (16 * ds + 8 * hl) * 2);
+      if (p.negate) qf[ds] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       dof[ds] = *(const u32x4*)(op + (16 * ds + 8 * hl) * 2);
     }
     // rows past Sq: P = 0 through lse2 = +inf
@@ -499,19 +505,28 @@ struct BwdDq {
     copy_tile<RB, 0, BN, 64 * NW>(vhead + r0 * p.v_ss * 2, p.v_ss * 2, p.Sk - r0, dst + TILE, tid);
   }
 
+  // tile j in buffer BUF (= j % 2, a compile-time value so that the LDS
+  // offsets fold into the instructions)
+  template <int B>
+  __device__ __forceinline__ void step(int j) {
+    wait_loads<0>();
+    lds_barrier();
+    if (j + 1 < ntiles) load_tile(j + 1, B ^ 1);
+    if (j <= jlast) tile<B>(j);
+  }
+
   __device__ __forceinline__ void run() {
     if (ntiles > 0) load_tile(0, 0);
-    for (int j = 0; j < ntiles; ++j) {
-      wait_loads<0>();
-      lds_barrier();
-      if (j + 1 < ntiles) load_tile(j + 1, (j + 1) & 1);
-      if (j <= jlast) tile(j, j & 1);
+    for (int j = 0; j < ntiles; j += 2) {
+      step<0>(j);
+      if (j + 1 < ntiles) step<1>(j + 1);
     }
     store();
   }
 
-  __device__ __forceinline__ void tile(int j, int buf) {
-    const uint32_t kb = lds0 + buf * BUF;
+  template <int B>
+  __device__ __forceinline__ void tile(int j) {
+    const uint32_t kb = lds0 + B * BUF;
     const uint32_t vb = kb + TILE;
     const int64_t kt0 = (int64_t)j * BN;
     uint32_t zm = 0;
@@ -525,22 +540,25 @@ struct BwdDq {
     // keys past Sk or above the diagonal: P = 0. Register r holds key
     // kt0 + 8*(r/4) + 4*hl + r%4.
     const bool need_mask = (kt0 + BN > p.Sk) || (CAUSAL && kt0 + BN - 1 > qw0 + p.moff);
-    int lim = BN;
     if (need_mask) {
+      // a real branch: tiles inside the keys and below the diagonal skip
+      // the compare-and-select on every score
+      asm volatile("");
       const int64_t kv = p.Sk - kt0;
-      lim = kv < BN ? (int)kv : BN;
+      int lim = kv < BN ? (int)kv : BN;
       if constexpr (CAUSAL) {
         int64_t qr = qrow + p.moff - kt0 + 1;
         if (qr < 0) qr = 0;
         lim = qr < lim ? (int)qr : lim;
       }
+      lim -= 4 * hl;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) >= lim ? -INFINITY : s[r];
     }
-    lim -= 4 * hl;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float x = __builtin_fmaf(s[r], p.c, -l2);
-      if (need_mask && (8 * (r >> 2) + (r & 3)) >= lim) x = -INFINITY;
-      const float pr = __builtin_amdgcn_exp2f(x);
+      // c > 0: a masked score (-inf) stays -inf
+      const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], p.c, -l2));
       if constexpr (DROP) {
         // register r holds Philox value r of this lane's block
         const float z = ((zm >> r) & 1u) ? p.inv_keep : 0.f;
@@ -738,7 +756,8 @@ static fa_status_t bwd_launch(const void* q, const void* k, const void* v, const
   p.H = (int32_t)H;
   p.Hkv = (int32_t)H_kv;
   p.scale = scale;
-  p.c = scale * fa::kLog2e;
+  p.c = fmaxf(fabsf(scale) * fa::kLog2e, FLT_MIN);
+  p.negate = scale < 0.f;
   const bool drop = keep_prob != 1.0f;
   p.seed = seed;
   p.rng_off = rng_off;

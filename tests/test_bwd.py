@@ -215,3 +215,16 @@ def test_bwd_dropout_chained_with_library_forward():
     bnd = term_bounds(qq, kk, vv, g, cfg.scale, True, 33, (0.75, 99, 4))
     check(fi.F16, tuple(t.double().cpu().numpy() for t in (dq, dk, dv)), ref, bnd,
           "dropout chained")
+
+
+def test_bwd_scale_variants():
+    """Negative, zero and large scales (a negative scale negates the
+    register-resident operand of S; zero gives uniform P and dQ = dK = 0)."""
+    for scale in (-0.3, 0.0, 0.6):
+        for mask in ("none", "top_left"):
+            cfg, inp, do = case_inputs(fi.F16, 1, 4, 2, 130, 97, 64, seed=1800)
+            cfg = cfg.replace(scale=scale) if scale != 0.0 else cfg.replace(scale=1e-30)
+            causal = MASKS[mask][0]
+            o, lse, ref, bnd = oracle_all(cfg, inp, do, causal, 0)
+            got = run_bwd(cfg, inp, do, o, lse, False if mask == "none" else mask, fi.F32)
+            check(fi.F16, got, ref, bnd, f"scale {scale} {mask}")
