@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 import fa_inputs as fi
-from oracle import attention_fp64, attention_rows_fp64
+from oracle import attention_fp64, attention_rows_fp64, dropout_keep_mask, head_forward
 
 # Tolerances on max |delta| against the fp64 oracle: 2e-3 on O and 1e-3 on
 # lse for fp16/bf16 inputs, 6e-2 on O for fp8 inputs (lse for fp8: 1e-3).
@@ -84,3 +84,27 @@ def oracle_rows(cfg: fi.Config, inp: fi.Inputs, b: int, h: int, rows):
     k = fi.as_float64(inp.k[b:b + 1, h:h + 1], inp.descale_k)
     v = fi.as_float64(inp.v[b:b + 1, h:h + 1], inp.descale_v)
     return attention_rows_fp64(q, k, v, cfg.scale, cfg.causal, 0, 0, rows)
+
+
+def term_bounds(q, k, v, g, scale, causal, off, drop=None):
+    """Largest sum of absolute term values per gradient tensor (drop: keep,
+    seed, offset of a dropout mask, whose Z / keep scales P in dV and dP)."""
+    B, H, Sq, D = q.shape
+    Hkv = k.shape[1]
+    bq = 0.0
+    bk = np.zeros(k.shape)
+    bv = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            kv = h // (H // Hkv)
+            _, _, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal, return_p=True,
+                                   offset=off)
+            z = 1.0
+            if drop is not None:
+                z = dropout_keep_mask(b * H + h, range(Sq), k.shape[2], *drop) / drop[0]
+            dp = (g[b, h] @ v[b, kv].T) * z
+            w = p * (np.abs(dp) + np.abs(np.sum(p * dp, axis=1, keepdims=True)))
+            bq = max(bq, float(np.max(abs(scale) * w @ np.abs(k[b, kv]))))
+            bk[b, kv] += abs(scale) * w.T @ np.abs(q[b, h])
+            bv[b, kv] += (p * z).T @ np.abs(g[b, h])
+    return bq, float(bk.max()), float(bv.max())

@@ -23,8 +23,8 @@ import torch
 
 import attention_fa_fwd_07_amd as fa
 import fa_inputs as fi
-from oracle import (attention_bwd_fp64, attention_dropout_fp64, attention_fp64,
-                    dropout_keep_mask, head_forward)
+from parity_util import term_bounds
+from oracle import attention_bwd_fp64, attention_dropout_fp64, attention_fp64
 
 pytestmark = pytest.mark.gpu
 
@@ -39,30 +39,6 @@ def case_inputs(dtype, B, H, Hkv, Sq, Sk, D, seed, amp=1.0):
     inp.v = inp.v[:, :Hkv].contiguous()
     do = fi.make_cotangent((B, H, Sq, D), dtype, seed + 5000)
     return cfg, inp, do
-
-
-def term_bounds(q, k, v, g, scale, causal, off, drop=None):
-    """Largest sum of absolute term values per gradient tensor (drop: keep,
-    seed, offset of a dropout mask, whose Z / keep scales P in dV and dP)."""
-    B, H, Sq, D = q.shape
-    Hkv = k.shape[1]
-    bq = 0.0
-    bk = np.zeros(k.shape)
-    bv = np.zeros(v.shape)
-    for b in range(B):
-        for h in range(H):
-            kv = h // (H // Hkv)
-            _, _, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal, return_p=True,
-                                   offset=off)
-            z = 1.0
-            if drop is not None:
-                z = dropout_keep_mask(b * H + h, range(Sq), k.shape[2], *drop) / drop[0]
-            dp = (g[b, h] @ v[b, kv].T) * z
-            w = p * (np.abs(dp) + np.abs(np.sum(p * dp, axis=1, keepdims=True)))
-            bq = max(bq, float(np.max(abs(scale) * w @ np.abs(k[b, kv]))))
-            bk[b, kv] += abs(scale) * w.T @ np.abs(q[b, h])
-            bv[b, kv] += (p * z).T @ np.abs(g[b, h])
-    return bq, float(bk.max()), float(bv.max())
 
 
 def oracle_all(cfg, inp, do, causal, off):
