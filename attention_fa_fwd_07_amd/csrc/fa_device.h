@@ -138,10 +138,20 @@ __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t 
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// max of two floats that are never NaN (scores, -inf, running maxima), as
+// one v_max_f32: fmaxf would first quiet possible signalling NaNs of
+// operands the compiler cannot see the origin of (a lane exchange, a loop
+// variable), one extra instruction per operand on every tile
+__device__ __forceinline__ float max_f32(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float wave_max_halves(float x) {
   // After the swap each lane holds its own value and its partner's (l ^ 32).
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  return max_f32(__uint_as_float(p[0]), __uint_as_float(p[1]));
 }
 __device__ __forceinline__ float wave_sum_halves(float x) {
   auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -164,6 +164,10 @@ struct FwdTile {
   uint32_t goff_k, goff_v;          // this lane's byte offsets in a full tile (first load)
   f32x16 acc_o[NDB];
   float m_run, l_run;
+  float neg_m;                      // -m_run, or 0 while m_run = -inf (the exponent's offset)
+  float thr;                        // m_run + the slack of the last move_ref (see there)
+  int jmask;                        // tiles j >= jmask need the key mask
+  int jfull;                        // tiles j < jfull lie wholly below Sk
 
   __device__ __forceinline__ FwdTile(const Params& pp, char* sm) : p(pp) {
     lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, sm);
@@ -242,6 +246,19 @@ struct FwdTile {
       jlast = jl < jlast ? (int)jl : jlast;
     }
     if (qw0 >= Sq) jlast = -1;   // all rows of this wave lie past Sq
+    {
+      // the first tile that reaches past Sk or, causal, past the diagonal
+      // of one of this wave's rows; the tiles before it need no mask
+      int64_t jm = Sk / BN;
+      if constexpr (CAUSAL) {
+        const int64_t x = qw0 + moff + 1 - BN;
+        const int64_t jc = x < 0 ? 0 : x / BN + 1;
+        jm = jc < jm ? jc : jm;
+      }
+      jmask = __builtin_amdgcn_readfirstlane(jm < ntiles ? (int)jm : ntiles);
+      const int64_t jf = Sk / BN;
+      jfull = __builtin_amdgcn_readfirstlane(jf < ntiles ? (int)jf : ntiles);
+    }
 
     // Q fragments (B operand of S^T = K Q^T), kept in registers; rows past
     // Sq read the last row (their results are never stored). Negative
@@ -311,6 +328,8 @@ struct FwdTile {
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc_o[db] = (f32x16){};
     m_run = -INFINITY;
+    neg_m = 0.f;
+    thr = -INFINITY;
     l_run = 0.f;
   }
 
@@ -323,12 +342,11 @@ struct FwdTile {
     const char* base = (IS_V ? vhead : khead) + row0 * kpitch;
     const uint32_t dst = lds0 + (IS_V ? NB + buf : buf) * TILE + wave * 64 * 16;
     const uint32_t goff = IS_V ? goff_v : goff_k;
-    const int64_t left = Sk - 1 - row0;
-    if (left >= BN - 1) {
+    if (j < jfull) {
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) dma16(base + (int64_t)i * (NT / C) * kpitch, goff, dst + i * NT * 16);
     } else {
-      const int rmax = (int)left;
+      const int rmax = (int)(Sk - 1 - row0);
 #pragma unroll
       for (int i = 0; i < LOADS; ++i) {
         const int pidx = i * NT + tid;
@@ -438,8 +456,7 @@ struct FwdTile {
     // mask: keys past Sk, keys above the diagonal. key = kt0 + kb*32 +
     // 8*(r/4) + 4*hl + r%4 is dead if it is >= Sk or > this row's query:
     // compare the compile-time part with a per-lane limit.
-    const bool need_mask = (kt0 + BN > Sk) || (CAUSAL && kt0 + BN - 1 > qw0 + moff);
-    if (need_mask) {
+    if (j >= jmask) {
       // keeps this a branch: full tiles (all but the last, or the diagonal
       // ones) then skip the compare-and-select on every score
       asm volatile("");
@@ -469,23 +486,41 @@ struct FwdTile {
     // that, a new maximum less than 2 above the reference keeps it (P then
     // stays below 4, its rounding stays relative), which skips the rescale
     // on most tiles of long rows.
+    move_ref(max_cand(s));
+  }
+
+  // this tile's row maximum in log2 units (scaled by c)
+  __device__ __forceinline__ float max_cand(const f32x16 (&s)[NKB]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
     mx = wave_max_halves(mx);
-    const float m_cand = fmaxf(m_run, mx * c);
-    // slack in log2 units; l of this lane's half of the keys bounds the
-    // row's l from below
-    const float slack = l_run >= 4.0f ? 2.0f : 0.0f;
-    if (__builtin_amdgcn_ballot_w64(m_cand > m_run + slack) != 0) {
-      const float m_new = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
+    return mx * c;
+  }
+
+  // Moves the reference when some row of the wave has a maximum mxc above
+  // m_run + slack, slack (log2 units) = 2 once this lane's half of l is at
+  // least 4 (it bounds the row's l from below), else 0. thr caches m_run +
+  // slack as of the last call that entered the branch: l only grows in
+  // between, so the cached slack is never larger than the current one and
+  // the cheap test below lets through every tile the exact test would; the
+  // exact test then decides, and refreshes thr.
+  __device__ __forceinline__ void move_ref(float mxc) {
+    if (__builtin_amdgcn_ballot_w64(mxc > thr) != 0) {
+      const float m_cand = max_f32(m_run, mxc);
+      const float slack = l_run >= 4.0f ? 2.0f : 0.0f;
+      if (__builtin_amdgcn_ballot_w64(m_cand > m_run + slack) != 0) {
+        const float m_new = (m_cand == -INFINITY) ? 0.f : m_cand;   // no (-inf) - (-inf)
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
-      m_run = m_cand;
+        for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+        m_run = m_cand;
+        neg_m = -m_new;
+      }
+      thr = m_run + (l_run >= 4.0f ? 2.0f : 0.0f);
     }
   }
 
@@ -503,7 +538,6 @@ struct FwdTile {
 
   __device__ __forceinline__ void exp_p(const f32x16 (&s)[NKB], u32x4 (&pf)[NST], u32x4 (&pl)[SPLIT_P ? NST : 1],
                                         const uint32_t (&dm)[8]) {
-    const float m_use = (m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
@@ -512,8 +546,8 @@ struct FwdTile {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 8 * half + 2 * e;
-          const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_use));
-          const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, -m_use));
+          const float x0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, neg_m));
+          const float x1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r + 1], c, neg_m));
           f[e] = pack2<MK>(x0, x1);
           l_run = add_pair<MK>(f[e], l_run);     // l sums the P that multiplies V
           if constexpr (SPLIT_P) {
