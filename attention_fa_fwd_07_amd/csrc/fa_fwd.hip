@@ -77,6 +77,8 @@ struct Params {
   const int32_t* cu_k;
   int32_t br;
   int32_t xcd_unit;     // > 0: launch-order groups dealt round-robin to the XCDs
+  int32_t qmajor;       // > 0 (causal): q-block-major order within each XCD, groups of qmajor heads
+  int32_t qsnake;       // with qmajor: the grid is resident at once; pair long and short blocks
   // dropout: the keep test of key j for query row i of query head bh uses
   // Philox4x64-10 keyed by (seed, rng_off); a kept P is scaled by inv_keep
   uint64_t seed, rng_off;
@@ -184,7 +186,10 @@ struct FwdTile {
     }
     bh = t / p.nqb;
     int qb = t - bh * p.nqb;
-    if constexpr (CAUSAL) qb = p.nqb - 1 - qb;   // longest rows first
+    if constexpr (CAUSAL) {
+      qb = p.nqb - 1 - qb;   // longest rows first
+      if (!SPLIT && p.qmajor > 0) qmajor_order(bh, qb);
+    }
     Sq = p.Sq;
     Sk = p.Sk;
     q0 = (int64_t)qb * BM;
@@ -331,6 +336,29 @@ struct FwdTile {
     neg_m = 0.f;
     thr = -INFINITY;
     l_run = 0.f;
+  }
+
+  // Causal launch order with whole groups of qmajor heads (the query heads
+  // that share a key/value head) dealt round-robin to the 8 XCDs: XCD x
+  // runs the groups x, x+8, ..., so each group's K/V stays in one L2.
+  // Within the XCD the blocks go by their number of key tiles across all
+  // of its heads: longest first when the grid takes several rounds of the
+  // CUs (a freed slot takes the longest block left); when the whole grid is
+  // resident at once (qsnake), the longer half in falling order and then
+  // the shorter half in rising order, so that the two blocks that share a
+  // CU (launch positions i and i + half) add up to about the same work.
+  __device__ __forceinline__ void qmajor_order(int& bh_out, int& qb_out) {
+    const int w = blockIdx.x;
+    const int xcd = w & 7, loc = w >> 3;
+    const int G = p.qmajor;
+    const int hx = p.total / p.nqb / 8;            // heads per XCD
+    const int half = p.qsnake ? (p.nqb / 2) * hx : p.total;
+    const int i = loc < half ? loc : loc - half;
+    const int rank = loc < half ? i / hx : p.nqb - 1 - i / hx;   // 0: the longest blocks
+    const int r = i - (i / hx) * hx;
+    const int gi = (r / G) * 8 + xcd;
+    bh_out = gi * G + r % G;
+    qb_out = p.nqb - 1 - rank;
   }
 
   // ---- HBM -> LDS: tile j of K or V into buffer buf (lanes 0..NT-1) ----
@@ -931,6 +959,12 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
   p.cu_k = nullptr;
   p.br = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT;
   p.xcd_unit = 0;
+  // causal: q-block-major order inside each XCD when whole key/value head
+  // groups divide evenly over the 8 XCDs; the resident-grid variant when
+  // every workgroup fits on the 256 CUs at once (three 4-wave or one
+  // 8-wave workgroup per CU)
+  p.qmajor = (causal && (B * Hkv) % 8 == 0) ? (int32_t)(H / Hkv) : 0;
+  p.qsnake = BH * nqb <= 256 * (nw == 4 ? 3 : 1);
   p.seed = 0;
   p.rng_off = 0;
   p.keep_thr = 0;
@@ -1141,6 +1175,8 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   p.moff = 0;
   p.nqb = (int32_t)nqb;
   p.total = (int32_t)(B * H * nqb);
+  p.qmajor = 0;
+  p.qsnake = 0;
   // sequences differ in work: deal each key/value head's blocks (else each
   // head's) round-robin to the 8 XCDs so they stay balanced and the blocks
   // sharing K/V still share one XCD's L2

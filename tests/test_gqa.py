@@ -7,7 +7,7 @@ import torch
 
 import attention_fa_fwd_07_amd as fa
 import fa_inputs as fi
-from oracle import attention_fp64
+from oracle import attention_fp64, attention_rows_fp64
 from parity_util import compare
 
 pytestmark = pytest.mark.gpu
@@ -104,3 +104,49 @@ def test_bshd_layout(dtype, D):
         assert np.all(o[empty] == 0.0) and np.all(np.isneginf(lse[empty]))
         compare(cfg, fi.F32, o[~empty], lse[~empty], ref_o[~empty], ref_l[~empty],
                 what=f"BSHD {dtype} D{D} H{H}/{Hkv} {Sq}x{Sk} {mask} splits {ns}")
+
+
+def _block_rows(Sq: int, bm: int):
+    """First, middle and last row of every block of bm query rows."""
+    rows = set()
+    for s in range(0, Sq, bm):
+        rows.update((s, min(s + bm // 2, Sq - 1), min(s + bm - 1, Sq - 1)))
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("D,B,H,Hkv,Sq,Sk,full", [
+    (128, 2, 8, 4, 700, 700, True),      # 96 workgroups: resident at once, long and short paired
+    (128, 2, 8, 4, 600, 700, True),      # the same with the diagonal shifted (bottom-right)
+    (128, 2, 16, 4, 3200, 3200, False),  # 800 workgroups of 4 waves: several rounds, longest first
+    (64, 2, 8, 4, 2000, 2000, True),     # 8-wave workgroups, resident at once
+    (64, 2, 8, 4, 5000, 5000, False),    # 8-wave workgroups, several rounds
+])
+def test_causal_launch_orders(D, B, H, Hkv, Sq, Sk, full):
+    """Causal grids whose groups of query heads sharing a key/value head
+    divide evenly over the 8 XCDs run in q-block-major order inside each
+    XCD (long and short blocks paired when the whole grid is resident,
+    longest first otherwise). Every (head, block) must still compute its own
+    rows: checked against the oracle on every row (full) or on the first,
+    middle and last row of every query block of every head."""
+    mask = "bottom_right" if Sq != Sk else "top_left"
+    cfg = fi.Config("order", B, H, Sq, Sk, D, fi.F16, True, seed=1200 + Sq + D)
+    inp = fi.make_inputs(cfg)
+    inp.k = inp.k[:, :Hkv].contiguous()
+    inp.v = inp.v[:, :Hkv].contiguous()
+    q64, k64, v64 = fi.values(inp)
+    offset = Sk - Sq
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    o, lse = fa.fa_fwd(q, k, v, scale=cfg.scale, causal=mask, o_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o = o.double().cpu().numpy()
+    lse = lse.double().cpu().numpy()
+    what = f"D{D} B{B} H{H}/{Hkv} {Sq}x{Sk} {mask}"
+    if full:
+        ref_o, ref_l = attention_fp64(q64, k64, v64, cfg.scale, True, offset)
+        compare(cfg, fi.F32, o, lse, ref_o, ref_l, what=what)
+        return
+    rows = _block_rows(Sq, 128)
+    for b in range(B):
+        for h in range(H):
+            ro, rl = attention_rows_fp64(q64, k64, v64, cfg.scale, True, b, h, rows, offset)
+            compare(cfg, fi.F32, o[b, h, rows], lse[b, h, rows], ro, rl, what=f"{what} b{b} h{h}")
