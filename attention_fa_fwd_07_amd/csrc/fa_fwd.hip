@@ -79,6 +79,7 @@ struct Params {
   int32_t xcd_unit;     // > 0: launch-order groups dealt round-robin to the XCDs
   int32_t qmajor;       // > 0 (causal): q-block-major order within each XCD, groups of qmajor heads
   int32_t qsnake;       // with qmajor: the grid is resident at once; pair long and short blocks
+  int32_t qrem;         // with qmajor: head groups beyond a multiple of 8, launched first
   // dropout: the keep test of key j for query row i of query head bh uses
   // Philox4x64-10 keyed by (seed, rng_off); a kept P is scaled by inv_keep
   uint64_t seed, rng_off;
@@ -347,14 +348,27 @@ struct FwdTile {
   // resident at once (qsnake), the longer half in falling order and then
   // the shorter half in rising order, so that the two blocks that share a
   // CU (launch positions i and i + half) add up to about the same work.
+  // The last qrem groups (the number of groups modulo 8) go first, longest
+  // blocks first, spread over the XCDs; the rest follow as above, each XCD
+  // offset by the same rotation.
   __device__ __forceinline__ void qmajor_order(int& bh_out, int& qb_out) {
-    const int w = blockIdx.x;
-    const int xcd = w & 7, loc = w >> 3;
     const int G = p.qmajor;
-    const int hx = p.total / p.nqb / 8;            // heads per XCD
+    const int BH = p.total / p.nqb;
+    const int hrem = p.qrem * G;                    // heads launched first
+    const int nrem = hrem * p.nqb;
+    int w = blockIdx.x;
+    if (w < nrem) {
+      const int rank = w / hrem;                    // 0: the longest blocks
+      bh_out = BH - hrem + (w - rank * hrem);
+      qb_out = p.nqb - 1 - rank;
+      return;
+    }
+    w -= nrem;
+    const int xcd = w & 7, loc = w >> 3;            // xcd: the XCD up to a fixed rotation
+    const int hx = (BH - hrem) / 8;                 // heads per XCD
     const int half = p.qsnake ? (p.nqb / 2) * hx : p.total;
     const int i = loc < half ? loc : loc - half;
-    const int rank = loc < half ? i / hx : p.nqb - 1 - i / hx;   // 0: the longest blocks
+    const int rank = loc < half ? i / hx : p.nqb - 1 - i / hx;
     const int r = i - (i / hx) * hx;
     const int gi = (r / G) * 8 + xcd;
     bh_out = gi * G + r % G;
@@ -959,12 +973,13 @@ fa_status_t check_call(const void* q, const void* k, const void* v, void* o, flo
   p.cu_k = nullptr;
   p.br = mask == FA_MASK_CAUSAL_BOTTOM_RIGHT;
   p.xcd_unit = 0;
-  // causal: q-block-major order inside each XCD when whole key/value head
-  // groups divide evenly over the 8 XCDs; the resident-grid variant when
-  // every workgroup fits on the 256 CUs at once (three 4-wave or one
-  // 8-wave workgroup per CU)
-  p.qmajor = (causal && (B * Hkv) % 8 == 0) ? (int32_t)(H / Hkv) : 0;
-  p.qsnake = BH * nqb <= 256 * (nw == 4 ? 3 : 1);
+  // causal: q-block-major order inside each XCD when there are at least 8
+  // key/value head groups; the resident-grid variant when they divide
+  // evenly over the XCDs and every workgroup fits on the 256 CUs at once
+  // (three 4-wave or one 8-wave workgroup per CU)
+  p.qmajor = (causal && B * Hkv >= 8) ? (int32_t)(H / Hkv) : 0;
+  p.qrem = (int32_t)((B * Hkv) % 8);
+  p.qsnake = p.qrem == 0 && BH * nqb <= 256 * (nw == 4 ? 3 : 1);
   p.seed = 0;
   p.rng_off = 0;
   p.keep_thr = 0;
@@ -1177,6 +1192,7 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   p.total = (int32_t)(B * H * nqb);
   p.qmajor = 0;
   p.qsnake = 0;
+  p.qrem = 0;
   // sequences differ in work: deal each key/value head's blocks (else each
   // head's) round-robin to the 8 XCDs so they stay balanced and the blocks
   // sharing K/V still share one XCD's L2

@@ -120,12 +120,15 @@ def _block_rows(Sq: int, bm: int):
     (128, 2, 16, 4, 3200, 3200, False),  # 800 workgroups of 4 waves: several rounds, longest first
     (64, 2, 8, 4, 2000, 2000, True),     # 8-wave workgroups, resident at once
     (64, 2, 8, 4, 5000, 5000, False),    # 8-wave workgroups, several rounds
+    (128, 3, 12, 12, 700, 700, True),    # 36 head groups: the 4 beyond a multiple of 8 go first
+    (64, 3, 6, 3, 2900, 3000, False),    # 9 groups of 2 heads, one beyond a multiple of 8
 ])
 def test_causal_launch_orders(D, B, H, Hkv, Sq, Sk, full):
-    """Causal grids whose groups of query heads sharing a key/value head
-    divide evenly over the 8 XCDs run in q-block-major order inside each
-    XCD (long and short blocks paired when the whole grid is resident,
-    longest first otherwise). Every (head, block) must still compute its own
+    """Causal grids with at least 8 groups of query heads sharing a
+    key/value head run in q-block-major order inside each XCD (long and
+    short blocks paired when the whole grid is resident and the groups
+    divide evenly over the XCDs, longest first otherwise; groups beyond a
+    multiple of 8 first). Every (head, block) must still compute its own
     rows: checked against the oracle on every row (full) or on the first,
     middle and last row of every query block of every head."""
     mask = "bottom_right" if Sq != Sk else "top_left"
