@@ -70,6 +70,11 @@ struct BwdParams {
   int32_t H, Hkv;
   int32_t nblk;         // blocks per head (dq) or per key/value head (dkv)
   int32_t total;        // workgroups of the launch
+  // causal launch order (xcd_lpt): qmajor > 0 orders the blocks by work
+  // across each XCD's heads, in groups of qmajor heads sharing K/V; qrem
+  // groups beyond a multiple of 8 go first; qsnake pairs long and short
+  // blocks when the whole grid is resident
+  int32_t qmajor, qrem, qsnake;
   float scale;          // S = scale * Q K^T (dQ and dK carry it with its sign)
   float c;              // max(|scale| * log2(e), FLT_MIN)
   int32_t negate;       // scale < 0: the register operand of S is negated (exact)
@@ -245,9 +250,14 @@ struct BwdDkv {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hl = lane >> 5;
     l32 = lane & 31;
-    const int t = xcd_remap(blockIdx.x, p.total);
-    const int bkv = t / p.nblk;
-    const int kb = t - bkv * p.nblk;
+    int bkv, kb;
+    if (CAUSAL && p.qmajor > 0) {   // key blocks by work across each XCD's heads (block 0 the most)
+      xcd_lpt(blockIdx.x, p.total, p.nblk, 1, p.qrem, p.qsnake != 0, bkv, kb);
+    } else {
+      const int t = xcd_remap(blockIdx.x, p.total);
+      bkv = t / p.nblk;
+      kb = t - bkv * p.nblk;
+    }
     b = bkv / p.Hkv;
     kvh = bkv - b * p.Hkv;
     group = p.H / p.Hkv;
@@ -457,10 +467,18 @@ struct BwdDq {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     hl = lane >> 5;
     l32 = lane & 31;
-    const int t = xcd_remap(blockIdx.x, p.total);
-    bh = t / p.nblk;
-    int qb = t - (int)bh * p.nblk;
-    if constexpr (CAUSAL) qb = p.nblk - 1 - qb;   // longest rows first
+    int qb;
+    if (CAUSAL && p.qmajor > 0) {   // query blocks by length across each XCD's heads
+      int u, rank;
+      xcd_lpt(blockIdx.x, p.total, p.nblk, p.qmajor, p.qrem, p.qsnake != 0, u, rank);
+      bh = u;
+      qb = p.nblk - 1 - rank;
+    } else {
+      const int t = xcd_remap(blockIdx.x, p.total);
+      bh = t / p.nblk;
+      qb = t - (int)bh * p.nblk;
+      if constexpr (CAUSAL) qb = p.nblk - 1 - qb;   // longest rows first
+    }
     const int b = (int)(bh / p.H);
     const int h = (int)(bh - (int64_t)b * p.H);
     const int kvh = h / (p.H / p.Hkv);
@@ -783,14 +801,23 @@ static fa_status_t bwd_launch(const void* q, const void* k, const void* v, const
   const int rpb = 256 / (int)(D / 8);
   hipLaunchKernelGGL(pre, dim3((unsigned)((rows + rpb - 1) / rpb)), dim3(256), 0, stream, p, rows);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
+  // causal grids with at least 8 key/value heads: blocks by work across
+  // each XCD's heads; pairing of long and short blocks when the groups
+  // divide over the XCDs and the grid is resident (two workgroups per CU)
+  const bool lpt = causal && B * H_kv >= 8;
+  p.qrem = (int32_t)((B * H_kv) % 8);
   BwdParams pk = p;
   pk.nblk = (int32_t)nkb;
   pk.total = (int32_t)(B * H_kv * nkb);
+  pk.qmajor = lpt ? 1 : 0;
+  pk.qsnake = lpt && p.qrem == 0 && pk.total <= 512;
   hipLaunchKernelGGL(dkv, dim3((unsigned)pk.total), dim3(256), 0, stream, pk);
   if (hipGetLastError() != hipSuccess) return FA_ERR_HIP;
   BwdParams pq = p;
   pq.nblk = (int32_t)nqb;
   pq.total = (int32_t)(B * H * nqb);
+  pq.qmajor = lpt ? (int32_t)(H / H_kv) : 0;
+  pq.qsnake = lpt && p.qrem == 0 && pq.total <= 512;
   hipLaunchKernelGGL(dq_fn, dim3((unsigned)pq.total), dim3(256), 0, stream, pq);
   return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -177,6 +177,38 @@ __device__ __forceinline__ int xcd_deal(int w, int unit) {
   return (xcd + 8 * g) * unit + (local - g * unit);
 }
 
+// Launch order for grids whose blocks differ in work (causal masks). The
+// grid holds total = U * nblk blocks: U units (heads) in groups of G that
+// read the same K/V, nblk blocks per unit, rank 0 being a unit's block with
+// the most work. Whole groups are dealt round-robin to the 8 XCDs (a
+// group's K/V stays in one L2) and each XCD runs its blocks by rank across
+// all of its units, not unit by unit: the most work first, so that a slot
+// freed late takes a short block; with snake (the whole grid resident at
+// once) the higher-work half in falling order and then the rest in rising
+// order, so that launch positions i and i + half, which share a CU, add up
+// to about the same work. The last rem groups (the group count modulo 8)
+// go first, most work first, spread over the XCDs; the others follow as
+// above with the XCDs rotated by a fixed amount.
+__device__ __forceinline__ void xcd_lpt(int w, int total, int nblk, int G, int rem, bool snake,
+                                        int& unit, int& rank) {
+  const int U = total / nblk;
+  const int urem = rem * G;
+  const int nrem = urem * nblk;
+  if (w < nrem) {
+    rank = w / urem;
+    unit = U - urem + (w - rank * urem);
+    return;
+  }
+  w -= nrem;
+  const int xcd = w & 7, loc = w >> 3;
+  const int ux = (U - urem) / 8;                  // units per XCD
+  const int half = snake ? (nblk / 2) * ux : total;
+  const int i = loc < half ? loc : loc - half;
+  rank = loc < half ? i / ux : nblk - 1 - i / ux;
+  const int r = i - (i / ux) * ux;
+  unit = ((r / G) * 8 + xcd) * G + r % G;
+}
+
 // Workgroup barrier for LDS hand-offs: waits for this wave's LDS operations
 // (lgkmcnt) but not for its HBM->LDS loads, which are waited for explicitly
 // (wait_loads) before the tile that reads them. The scheduling fences keep

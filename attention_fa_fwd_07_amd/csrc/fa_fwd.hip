@@ -77,9 +77,11 @@ struct Params {
   const int32_t* cu_k;
   int32_t br;
   int32_t xcd_unit;     // > 0: launch-order groups dealt round-robin to the XCDs
-  int32_t qmajor;       // > 0 (causal): q-block-major order within each XCD, groups of qmajor heads
-  int32_t qsnake;       // with qmajor: the grid is resident at once; pair long and short blocks
-  int32_t qrem;         // with qmajor: head groups beyond a multiple of 8, launched first
+  // causal launch order (xcd_lpt): qmajor > 0 orders the blocks by length
+  // across each XCD's heads, in groups of qmajor heads sharing K/V; qrem
+  // groups beyond a multiple of 8 go first; qsnake pairs long and short
+  // blocks when the whole grid is resident
+  int32_t qmajor, qrem, qsnake;
   // dropout: the keep test of key j for query row i of query head bh uses
   // Philox4x64-10 keyed by (seed, rng_off); a kept P is scaled by inv_keep
   uint64_t seed, rng_off;
@@ -189,7 +191,11 @@ struct FwdTile {
     int qb = t - bh * p.nqb;
     if constexpr (CAUSAL) {
       qb = p.nqb - 1 - qb;   // longest rows first
-      if (!SPLIT && p.qmajor > 0) qmajor_order(bh, qb);
+      if (!SPLIT && p.qmajor > 0) {   // blocks by length across each XCD's heads
+        int rank;
+        xcd_lpt(blockIdx.x, p.total, p.nqb, p.qmajor, p.qrem, p.qsnake != 0, bh, rank);
+        qb = p.nqb - 1 - rank;
+      }
     }
     Sq = p.Sq;
     Sk = p.Sk;
@@ -337,42 +343,6 @@ struct FwdTile {
     neg_m = 0.f;
     thr = -INFINITY;
     l_run = 0.f;
-  }
-
-  // Causal launch order with whole groups of qmajor heads (the query heads
-  // that share a key/value head) dealt round-robin to the 8 XCDs: XCD x
-  // runs the groups x, x+8, ..., so each group's K/V stays in one L2.
-  // Within the XCD the blocks go by their number of key tiles across all
-  // of its heads: longest first when the grid takes several rounds of the
-  // CUs (a freed slot takes the longest block left); when the whole grid is
-  // resident at once (qsnake), the longer half in falling order and then
-  // the shorter half in rising order, so that the two blocks that share a
-  // CU (launch positions i and i + half) add up to about the same work.
-  // The last qrem groups (the number of groups modulo 8) go first, longest
-  // blocks first, spread over the XCDs; the rest follow as above, each XCD
-  // offset by the same rotation.
-  __device__ __forceinline__ void qmajor_order(int& bh_out, int& qb_out) {
-    const int G = p.qmajor;
-    const int BH = p.total / p.nqb;
-    const int hrem = p.qrem * G;                    // heads launched first
-    const int nrem = hrem * p.nqb;
-    int w = blockIdx.x;
-    if (w < nrem) {
-      const int rank = w / hrem;                    // 0: the longest blocks
-      bh_out = BH - hrem + (w - rank * hrem);
-      qb_out = p.nqb - 1 - rank;
-      return;
-    }
-    w -= nrem;
-    const int xcd = w & 7, loc = w >> 3;            // xcd: the XCD up to a fixed rotation
-    const int hx = (BH - hrem) / 8;                 // heads per XCD
-    const int half = p.qsnake ? (p.nqb / 2) * hx : p.total;
-    const int i = loc < half ? loc : loc - half;
-    const int rank = loc < half ? i / hx : p.nqb - 1 - i / hx;
-    const int r = i - (i / hx) * hx;
-    const int gi = (r / G) * 8 + xcd;
-    bh_out = gi * G + r % G;
-    qb_out = p.nqb - 1 - rank;
   }
 
   // ---- HBM -> LDS: tile j of K or V into buffer buf (lanes 0..NT-1) ----

@@ -204,3 +204,20 @@ def test_bwd_scale_variants():
             o, lse, ref, bnd = oracle_all(cfg, inp, do, causal, 0)
             got = run_bwd(cfg, inp, do, o, lse, False if mask == "none" else mask, fi.F32)
             check(fi.F16, got, ref, bnd, f"scale {scale} {mask}")
+
+
+@pytest.mark.parametrize("D,B,H,Hkv,Sq,Sk,mask", [
+    (128, 2, 8, 4, 700, 700, "top_left"),       # 8 groups: resident grids, long and short paired
+    (64, 2, 8, 8, 600, 800, "bottom_right"),    # 16 key/value heads, diagonal shifted
+    (128, 3, 6, 3, 1000, 1000, "top_left"),     # 9 groups: the one beyond a multiple of 8 first
+    (64, 2, 16, 8, 2200, 2200, "top_left"),     # dQ: 544 workgroups, several rounds
+])
+def test_bwd_causal_launch_orders(D, B, H, Hkv, Sq, Sk, mask):
+    """Causal backward grids with at least 8 key/value heads order the
+    key blocks (dK/dV kernel) and query blocks (dQ kernel) by work across
+    each XCD's heads; every gradient must still land on its own rows."""
+    cfg, inp, do = case_inputs(fi.F16, B, H, Hkv, Sq, Sk, D, seed=1300 + Sq + D)
+    off = (Sk - Sq) if mask == "bottom_right" else 0
+    o, lse, ref, bounds = oracle_all(cfg, inp, do, True, off)
+    got = run_bwd(cfg, inp, do, o, lse, mask, fi.F32)
+    check(fi.F16, got, ref, bounds, f"D{D} B{B} H{H}/{Hkv} {Sq}x{Sk} {mask}")
