@@ -241,6 +241,20 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // their halves with words 1 and 3 and the key; the key advances by the two
 // Weyl constants between rounds. c is the counter on entry, the output on
 // return.
+// The 128-bit product m * c as (lo, hi) from four 32 x 32 + 64 -> 64-bit
+// multiply-adds (v_mad_u64_u32): with m = mh:ml and c = ch:cl,
+// t = cl*mh + hi(cl*ml) and t2 = ch*ml + lo(t) cannot overflow, lo =
+// lo(cl*ml) + 2^32 lo(t2) and hi = ch*mh + hi(t) + hi(t2).
+__device__ __forceinline__ void mul64wide(uint64_t m, uint64_t c, uint64_t& lo, uint64_t& hi) {
+  const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32);
+  const uint32_t cl = (uint32_t)c, ch = (uint32_t)(c >> 32);
+  const uint64_t p0 = (uint64_t)cl * ml;
+  const uint64_t t = (uint64_t)cl * mh + (p0 >> 32);
+  const uint64_t t2 = (uint64_t)ch * ml + (uint32_t)t;
+  lo = (uint32_t)p0 | (t2 << 32);
+  hi = (uint64_t)ch * mh + ((t >> 32) + (t2 >> 32));
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uint64_t k1) {
   constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
   constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
@@ -250,8 +264,9 @@ __device__ __forceinline__ void philox4x64_10(uint64_t (&c)[4], uint64_t k0, uin
       k0 += W0;
       k1 += W1;
     }
-    const uint64_t lo0 = M0 * c[0], hi0 = __umul64hi(M0, c[0]);
-    const uint64_t lo1 = M1 * c[2], hi1 = __umul64hi(M1, c[2]);
+    uint64_t lo0, hi0, lo1, hi1;
+    mul64wide(M0, c[0], lo0, hi0);
+    mul64wide(M1, c[2], lo1, hi1);
     c[0] = hi1 ^ c[1] ^ k0;
     c[1] = lo1;
     c[2] = hi0 ^ c[3] ^ k1;
