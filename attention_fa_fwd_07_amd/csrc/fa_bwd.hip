@@ -244,7 +244,7 @@ struct BwdDkv {
   f32x16 acc_k[NDB], acc_v[NDB];
 
   __device__ __forceinline__ BwdDkv(const BwdParams& p_, char* smem) : p(p_) {
-    lds0 = (uint32_t)(uintptr_t)smem;
+    lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, smem);
     tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -459,9 +459,13 @@ struct BwdDq {
   float l2, dl;
   u32x4 qf[NDS], dof[NDS];
   f32x16 acc[NDB];
+  // LDS addresses of this lane's fragments in buffer 0 (the buffer and the
+  // 16-key step go into the reads' immediate offsets): K and V row
+  // fragments per k-step, transposed K fragments per head-dim block and read
+  uint32_t ka[NDS], va[NDS], ta[NDB][2];
 
   __device__ __forceinline__ BwdDq(const BwdParams& p_, char* smem) : p(p_) {
-    lds0 = (uint32_t)(uintptr_t)smem;
+    lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, smem);
     tid = threadIdx.x;
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -514,6 +518,15 @@ struct BwdDq {
     dl = qrow < p.Sq ? p.delta[bh * p.Sqp + qrow] : 0.f;
 #pragma unroll
     for (int db = 0; db < NDB; ++db) acc[db] = (f32x16){};
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      ka[ds] = lds0 + l32 * RB + (((2 * ds + hl) ^ swz<RB, 1>(l32)) << 4);
+      va[ds] = lds0 + TILE + l32 * RB + (((2 * ds + hl) ^ swz<RB, 0>(l32)) << 4);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) ta[db][e] = tr_addr<RB, 1>(lds0, lane, hl, db, e);
   }
 
   __device__ __forceinline__ void load_tile(int j, int buf) {
@@ -544,17 +557,16 @@ struct BwdDq {
 
   template <int B>
   __device__ __forceinline__ void tile(int j) {
-    const uint32_t kb = lds0 + B * BUF;
-    const uint32_t vb = kb + TILE;
+    constexpr uint32_t off = B * BUF;
     const int64_t kt0 = (int64_t)j * BN;
     uint32_t zm = 0;
     if constexpr (DROP) zm = keep_bits16((uint64_t)(2 * j + hl), (uint64_t)qrow, (uint64_t)bh, p);
     // S^T = K Q^T, dP^T = V dO^T: lane = query (l32), rows = keys
     f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) s = mfma32<KIND>(row_frag<RB, 1>(kb, l32, ds, hl), qf[ds], s);
+    for (int ds = 0; ds < NDS; ++ds) s = mfma32<KIND>(lds_load<u32x4>(ka[ds] + off), qf[ds], s);
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) dp = mfma32<KIND>(row_frag<RB, 0>(vb, l32, ds, hl), dof[ds], dp);
+    for (int ds = 0; ds < NDS; ++ds) dp = mfma32<KIND>(lds_load<u32x4>(va[ds] + off), dof[ds], dp);
     // keys past Sk or above the diagonal: P = 0. Register r holds key
     // kt0 + 8*(r/4) + 4*hl + r%4.
     const bool need_mask = (kt0 + BN > p.Sk) || (CAUSAL && kt0 + BN - 1 > qw0 + p.moff);
@@ -591,8 +603,8 @@ struct BwdDq {
       const u32x4 dsf = pack8<KIND>(dp, st);
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint32_t so = st * 16 * RB;
-        const u32x4 a = tr_frag(tr_addr<RB, 1>(kb + so, lane, hl, db, 0), tr_addr<RB, 1>(kb + so, lane, hl, db, 1));
+        const uint32_t so = off + st * 16 * RB;
+        const u32x4 a = tr_frag(ta[db][0] + so, ta[db][1] + so);
         acc[db] = mfma32<KIND>(a, dsf, acc[db]);
       }
     }
