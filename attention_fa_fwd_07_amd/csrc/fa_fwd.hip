@@ -587,11 +587,18 @@ struct FwdTile {
   // ---- O^T += V^T P^T for one tile (buffer BUF); the V fragments of step
   // st+1 are read while the MFMAs of step st run ----
   template <int BUF>
-  __device__ __forceinline__ void gemm_pv(const u32x4 (&pf)[NST], const u32x4 (&pl)[SPLIT_P ? NST : 1]) {
+  __device__ __forceinline__ void read_v0(u32x4 (&v0)[NDB]) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) v0[db] = v_frag(BUF * TILE, 0, db);
+  }
+
+  template <int BUF>
+  __device__ __forceinline__ void gemm_pv(const u32x4 (&pf)[NST], const u32x4 (&pl)[SPLIT_P ? NST : 1],
+                                          const u32x4 (&v0)[NDB]) {
     constexpr uint32_t voff = BUF * TILE;
     u32x4 vf[2][NDB];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) vf[0][db] = v_frag(voff, 0, db);
+    for (int db = 0; db < NDB; ++db) vf[0][db] = v0[db];
 #pragma unroll
     for (int st = 0; st < NST; ++st) {
       if (st + 1 < NST) {
@@ -615,8 +622,15 @@ struct FwdTile {
     uint32_t dm[8];
     if constexpr (DROP) drop_masks(j, dm);
     gemm_s<BUF>(s);
+    // plain instances: the first 16-key step's V fragments are read before
+    // the softmax, so their LDS latency runs during it (the split and
+    // dropout instances have no registers to spare for them)
+    constexpr bool EARLY_V = !SPLIT && !DROP;
+    u32x4 v0[NDB];
+    if constexpr (EARLY_V) read_v0<BUF>(v0);
     softmax(j, s, pf, pl, dm);
-    gemm_pv<BUF>(pf, pl);
+    if constexpr (!EARLY_V) read_v0<BUF>(v0);
+    gemm_pv<BUF>(pf, pl, v0);
   }
 
   template <int BUF>
