@@ -118,8 +118,8 @@ def _block_rows(Sq: int, bm: int):
     (128, 2, 8, 4, 700, 700, True),      # 96 workgroups: resident at once, long and short paired
     (128, 2, 8, 4, 600, 700, True),      # the same with the diagonal shifted (bottom-right)
     (128, 2, 16, 4, 3200, 3200, False),  # 800 workgroups of 4 waves: several rounds, longest first
-    (64, 2, 8, 4, 2000, 2000, True),     # 8-wave workgroups, resident at once
-    (64, 2, 8, 4, 5000, 5000, False),    # 8-wave workgroups, several rounds
+    (64, 2, 8, 4, 2000, 2000, True),     # D = 64 (64-key tiles), resident at once
+    (64, 2, 8, 4, 7000, 7000, False),    # D = 64, 880 workgroups: several rounds
     (128, 3, 12, 12, 700, 700, True),    # 36 head groups: the 4 beyond a multiple of 8 go first
     (64, 3, 6, 3, 2900, 3000, False),    # 9 groups of 2 heads, one beyond a multiple of 8
 ])
