@@ -567,6 +567,18 @@ struct BwdDq {
     for (int ds = 0; ds < NDS; ++ds) s = mfma32<KIND>(lds_load<u32x4>(ka[ds] + off), qf[ds], s);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds) dp = mfma32<KIND>(lds_load<u32x4>(va[ds] + off), dof[ds], dp);
+    // the transposed K fragments of dQ^T += K^T dS^T: without dropout read
+    // now, so that their LDS latency runs during the exponentials below (the
+    // dropout instances have no registers to spare for them)
+    u32x4 kt[2][NDB];
+    auto read_kt = [&]() {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+          kt[st][db] = tr_frag(ta[db][0] + off + st * 16 * RB, ta[db][1] + off + st * 16 * RB);
+    };
+    if constexpr (!DROP) read_kt();
     // keys past Sk or above the diagonal: P = 0. Register r holds key
     // kt0 + 8*(r/4) + 4*hl + r%4.
     const bool need_mask = (kt0 + BN > p.Sk) || (CAUSAL && kt0 + BN - 1 > qw0 + p.moff);
@@ -598,15 +610,12 @@ struct BwdDq {
       }
     }
     // dQ^T += K^T dS^T
+    if constexpr (DROP) read_kt();
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       const u32x4 dsf = pack8<KIND>(dp, st);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint32_t so = off + st * 16 * RB;
-        const u32x4 a = tr_frag(ta[db][0] + so, ta[db][1] + so);
-        acc[db] = mfma32<KIND>(a, dsf, acc[db]);
-      }
+      for (int db = 0; db < NDB; ++db) acc[db] = mfma32<KIND>(kt[st][db], dsf, acc[db]);
     }
   }
 
