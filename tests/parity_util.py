@@ -86,25 +86,84 @@ def oracle_rows(cfg: fi.Config, inp: fi.Inputs, b: int, h: int, rows):
     return attention_rows_fp64(q, k, v, cfg.scale, cfg.causal, 0, 0, rows)
 
 
-def term_bounds(q, k, v, g, scale, causal, off, drop=None):
-    """Largest sum of absolute term values per gradient tensor (drop: keep,
-    seed, offset of a dropout mask, whose Z / keep scales P in dV and dP)."""
+def grad_bounds(q, k, v, g, scale, causal, off, drop=None, o_used=None, lse_used=None):
+    """Per-element error bounds of dQ, dK and dV, as (T, E) per tensor.
+
+    T: the sum of the absolute values of the terms of each gradient element
+    that the kernels round to the input type before a product: P in
+    dV = P^T dO, dS = P (dP - Delta) in dQ = scale dS K and dK = scale dS^T Q
+    (|dS| <= P (|dP| + |Delta|)); the comparison allows TOL * T.
+    E: the exact propagation of what the kernels are given that differs from
+    the oracle's own values: Delta = rowsum(dO * O) formed from the O they
+    receive (o_used, e.g. the oracle's O rounded to the input type, or the
+    library's forward output), and P recomputed from the lse they receive
+    (lse_used). drop: (keep, seed, offset) of a dropout mask, whose Z / keep
+    scales P in dV and dP. Inputs are float64 numpy arrays."""
     B, H, Sq, D = q.shape
     Hkv = k.shape[1]
-    bq = 0.0
-    bk = np.zeros(k.shape)
-    bv = np.zeros(v.shape)
+    T = [np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)]
+    E = [np.zeros(q.shape), np.zeros(k.shape), np.zeros(v.shape)]
+    sc = abs(scale)
     for b in range(B):
         for h in range(H):
             kv = h // (H // Hkv)
-            _, _, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal, return_p=True,
-                                   offset=off)
+            _, lse_ex, p = head_forward(q[b, h], k[b, kv], v[b, kv], scale, causal, return_p=True,
+                                        offset=off)
             z = 1.0
             if drop is not None:
                 z = dropout_keep_mask(b * H + h, range(Sq), k.shape[2], *drop) / drop[0]
+            pz = p * z
+            o_ex = pz @ v[b, kv]
             dp = (g[b, h] @ v[b, kv].T) * z
-            w = p * (np.abs(dp) + np.abs(np.sum(p * dp, axis=1, keepdims=True)))
-            bq = max(bq, float(np.max(abs(scale) * w @ np.abs(k[b, kv]))))
-            bk[b, kv] += abs(scale) * w.T @ np.abs(q[b, h])
-            bv[b, kv] += (p * z).T @ np.abs(g[b, h])
-    return bq, float(bk.max()), float(bv.max())
+            delta = np.sum(p * dp, axis=1, keepdims=True)
+            aq, ak = np.abs(q[b, h]), np.abs(k[b, kv])
+            w = p * (np.abs(dp) + np.abs(delta))
+            T[0][b, h] = sc * w @ ak
+            T[1][b, kv] += sc * w.T @ aq
+            T[2][b, kv] += pz.T @ np.abs(g[b, h])
+            if o_used is not None:
+                dd = np.abs(np.sum(g[b, h] * (o_used[b, h] - o_ex), axis=1, keepdims=True))
+                E[0][b, h] += sc * dd * (p @ ak)
+                E[1][b, kv] += sc * p.T @ (dd * aq)
+            if lse_used is not None:
+                both_empty = np.isneginf(lse_ex) & np.isneginf(lse_used[b, h])
+                d = np.where(both_empty, 0.0, lse_ex - lse_used[b, h])
+                eps = np.abs(np.expm1(d))[:, None]
+                ds = np.abs(p * (dp - delta)) * eps
+                E[0][b, h] += sc * ds @ ak
+                E[1][b, kv] += sc * ds.T @ aq
+                E[2][b, kv] += (pz * eps).T @ np.abs(g[b, h])
+    return tuple(zip(T, E))
+
+
+def check_grads(dtype, got, ref, bounds, what, grad_dtype=None):
+    """Assert |g - g_ref| <= TOL * T + E (+ one unit in the last place of a
+    16-bit gradient type) element by element; returns, per tensor, the
+    largest fraction of its element's allowance an error uses."""
+    tol = TOL_GRAD[dtype]
+    out = []
+    for name, gv, r, (t, e) in zip(("dq", "dk", "dv"), got, ref, bounds):
+        assert np.all(np.isfinite(gv)), f"{what}: non-finite {name}"
+        err = np.abs(gv - r)
+        floor = 2.0 ** -24 * float(np.max(t, initial=0.0))
+        lim = tol * t + 1.01 * e + floor
+        if grad_dtype is not None and grad_dtype != fi.F32:
+            lim = lim + ulp(r, grad_dtype)
+        bad = err > lim
+        assert not np.any(bad), (
+            f"{what}: {name} exceeds its element bound at {np.argwhere(bad)[:4].tolist()}: "
+            f"err {err[bad][:4].tolist()} bound {lim[bad][:4].tolist()}")
+        out.append(float(np.max(err / lim, initial=0.0)))
+    return out
+
+
+# rounding-term tolerance of the backward: 2u (fp16 u = 2^-11, bf16 2^-8)
+TOL_GRAD = {fi.F16: 2 * 2.0 ** -11, fi.BF16: 2 * 2.0 ** -8}
+
+
+def as_used(x: np.ndarray, dtype: str) -> np.ndarray:
+    """x as the kernels receive it: float64 -> float32 -> dtype, back to float64."""
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32)
+    if dtype != fi.F32:
+        t = t.to(fi.TORCH_DTYPE[dtype])
+    return t.double().numpy()

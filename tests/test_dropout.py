@@ -139,3 +139,87 @@ def test_dropout_determinism_and_keep_one():
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(l1.view(torch.int32), l2.view(torch.int32))
+
+
+def _bit_planes(S: int, D: int, lo: int) -> np.ndarray:
+    """[S, D]: column d holds 2^(t - lo) at the indices t*D + d with
+    lo <= t < lo + 16, and 0 elsewhere (16 distinct powers of two per
+    column, each below 2^16, so their sums are exact in fp16 inputs and an
+    fp32 accumulator)."""
+    x = np.zeros((S, D))
+    j = np.arange(S)
+    t = j // D - lo
+    sel = (t >= 0) & (t < 16)
+    x[j[sel], j[sel] % D] = 2.0 ** t[sel]
+    return x
+
+
+def _decode(x: np.ndarray) -> np.ndarray:
+    """Integer codes x [R, D] (< 2^16) -> bits [R, 16, D]."""
+    c = np.rint(x).astype(np.int64)
+    return (c[:, None, :] >> np.arange(16)[None, :, None]) & 1
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_forward_every_keep_bit(D):
+    """Every keep bit of every row of six heads at Sq = Sk = 4096 against the
+    oracle's mask. With Q = 0 every score is 0, so P = 2^-12 exactly for
+    every key; V (_bit_planes) gives key t*D + d the value 2^(t - lo) in
+    column d, so O[i, d] * Sk * keep_prob is the integer whose bit t - lo is
+    the keep bit of key t*D + d. One wrong bit changes an output by at least
+    2^-12 / keep_prob, while the arithmetic here is exact up to one fp32
+    rounding."""
+    B, H, S, keep, seed, off = 2, 3, 4096, 0.8, 1234, 77
+    q = torch.zeros(B, H, S, D, dtype=torch.float16, device="cuda")
+    k = torch.zeros(B, H, S, D, dtype=torch.float16, device="cuda")
+    ref = {(b, h): oracle_mask(b * H + h, S, keep, seed, off) for b in range(B) for h in range(H)}
+    for lo in range(0, S // D, 16):
+        vp = torch.from_numpy(_bit_planes(S, D, lo)).to(torch.float16)
+        v = vp.expand(B, H, S, D).contiguous().cuda()
+        o, _ = fa.fa_fwd(q, k, v, scale=D ** -0.5, keep_prob=keep, seed=seed, rng_offset=off,
+                         o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        o = o.double().cpu().numpy() * S * keep
+        for b in range(B):
+            for h in range(H):
+                bits = _decode(o[b, h])                                   # [Sq, 16, D]
+                want = ref[(b, h)][:, lo * D:(lo + 16) * D].reshape(S, 16, D)
+                bad = np.argwhere(bits != want)
+                assert bad.size == 0, (
+                    f"D{D} head ({b},{h}): keep bits differ at (row, key) "
+                    f"{[(int(r), int((lo + t) * D + d)) for r, t, d in bad[:5]]}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_every_keep_bit(D):
+    """The same through dV = (P Z / keep)^T dO of fa_bwd_dropout: with Q = 0
+    and lse = ln Sk every P is 2^-12, keep_prob 0.5 makes P / keep_prob a
+    power of two too, and dO (_bit_planes over the query rows) gives row
+    t*D + d the value 2^(t - lo) in column d, so dV[j, d] * Sq * keep_prob is
+    the integer whose bit t - lo is the keep bit of (row t*D + d, key j)."""
+    B, H, S, keep, seed, off = 1, 2, 4096, 0.5, 4321, 9
+    q = torch.zeros(B, H, S, D, dtype=torch.float16, device="cuda")
+    k = torch.zeros(B, H, S, D, dtype=torch.float16, device="cuda")
+    v = torch.zeros(B, H, S, D, dtype=torch.float16, device="cuda")
+    o = torch.zeros(B, H, S, D, dtype=torch.float16, device="cuda")
+    lse = torch.full((B, H, S), float(np.log(S)), dtype=torch.float32, device="cuda")
+    ref = {h: oracle_mask(h, S, keep, seed, off) for h in range(H)}
+    for lo in range(0, S // D, 16):
+        gp = torch.from_numpy(_bit_planes(S, D, lo)).to(torch.float16)
+        do = gp.expand(B, H, S, D).contiguous().cuda()
+        _, _, dv = fa.fa_bwd(q, k, v, o, do, lse, scale=D ** -0.5, keep_prob=keep, seed=seed,
+                             rng_offset=off, grad_dtype=torch.float32)
+        torch.cuda.synchronize()
+        dv = dv.double().cpu().numpy() * S * keep
+        for h in range(H):
+            bits = _decode(dv[0, h])                                     # [Sk, 16, D]
+            want = ref[h][lo * D:(lo + 16) * D, :].reshape(16, D, S).transpose(2, 0, 1)
+            bad = np.argwhere(bits != want)
+            assert bad.size == 0, (
+                f"D{D} head {h}: keep bits differ at (row, key) "
+                f"{[(int((lo + t) * D + d), int(j)) for j, t, d in bad[:5]]}")
+
+
+def oracle_mask(bh: int, S: int, keep: float, seed: int, off: int) -> np.ndarray:
+    from oracle import dropout_keep_mask
+    return dropout_keep_mask(bh, range(S), S, keep, seed, off)

@@ -9,7 +9,7 @@ import torch
 import attention_fa_fwd_07_amd as fa
 import fa_inputs as fi
 from oracle import attention_bwd_fp64, attention_fp64, attention_varlen_fp64
-from parity_util import TOL_LSE, TOL_O, term_bounds, to_device, ulp
+from parity_util import TOL_LSE, TOL_O, as_used, check_grads, grad_bounds, to_device, ulp
 
 pytestmark = pytest.mark.gpu
 
@@ -116,13 +116,9 @@ def test_random_causal_many_heads(case):
                            grad_dtype=torch.float32)
     torch.cuda.synchronize()
     refs = attention_bwd_fp64(q64, k64, v64, g.double().numpy(), cfg.scale, True, off)
-    bounds = term_bounds(q64, k64, v64, g.double().numpy(), cfg.scale, True, off)
-    u = 2 * (2.0 ** -11 if dtype == fi.F16 else 2.0 ** -8)
-    for name, got, ref, bnd in zip(("dq", "dk", "dv"), (dq, dk, dv), refs, bounds):
-        got = got.double().cpu().numpy()
-        scl = max(bnd, np.max(np.abs(ref), initial=0.0), 1e-30)
-        e = np.max(np.abs(got - ref), initial=0.0) / scl
-        assert e <= u, f"{what}: {name} rel err {e:.3e}"
+    bounds = grad_bounds(q64, k64, v64, g.double().numpy(), cfg.scale, True, off,
+                         o_used=as_used(ref_o, dtype), lse_used=as_used(ref_l, fi.F32))
+    check_grads(dtype, tuple(t.double().cpu().numpy() for t in (dq, dk, dv)), refs, bounds, what)
 
 
 @pytest.mark.parametrize("case", range(12))
@@ -195,12 +191,6 @@ def test_random_backward(case):
     grads = fa.fa_bwd(q, k, v, o, do.cuda(), lse, scale=cfg.scale,
                       causal=False if mask == "none" else mask, grad_dtype=torch.float32)
     torch.cuda.synchronize()
-    u = 2.0 ** -11 if dtype == fi.F16 else 2.0 ** -8
-    bnd = term_bounds(q64, k64, v64, do.double().numpy(), cfg.scale, mask != "none", off)
-    for name, g, r, b in zip(("dq", "dk", "dv"), grads, ref, bnd):
-        g = g.double().cpu().numpy()
-        assert np.all(np.isfinite(g)), (what, name)
-        # the bound of the backward parity tests: 2u times the largest sum
-        # of absolute term values of the tensor
-        e = np.abs(g - r).max() / max(b, np.abs(r).max(), 1e-30)
-        assert e <= 2 * u, (what, name, e)
+    bnd = grad_bounds(q64, k64, v64, do.double().numpy(), cfg.scale, mask != "none", off,
+                      o_used=as_used(o_ref, dtype), lse_used=as_used(lse_ref, fi.F32))
+    check_grads(dtype, tuple(t.double().cpu().numpy() for t in grads), ref, bnd, what)
