@@ -227,6 +227,53 @@ def fa_fwd(q, k, v, *, scale: float | None = None, causal: bool = False,
                  out, lse, stream, None, None, layout)
 
 
+def _check_buffer(name, t, shape, dtypes, device):
+    """A caller-supplied buffer must be a contiguous GPU tensor on ``device``
+    with exactly ``shape`` and a dtype in ``dtypes``: the C ABI takes bare
+    pointers and cannot check sizes, so a short or misplaced buffer would be
+    written or read out of bounds."""
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device}, not {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in dtypes)}, not {t.dtype}")
+
+
+def _check_inputs(names_tensors):
+    """q, k, v (and the like): contiguous GPU tensors on one device."""
+    dev = None
+    for name, t in names_tensors:
+        if not getattr(t, "is_cuda", False):
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} must be on {dev}, not {t.device}")
+    return dev
+
+
+def _check_descales(ds, dev):
+    import torch
+    for name, t in zip(("descale_q", "descale_k", "descale_v"), ds):
+        if t is not None:
+            _check_buffer(name, t, tuple(t.shape), (torch.float32,), dev)
+            if t.numel() != 1:
+                raise ValueError(f"{name} must hold exactly one float32")
+
+
+def _check_workspace(ws, dev):
+    import torch
+    if ws is not None:
+        _check_buffer("workspace", ws, (ws.numel(),), (torch.uint8,), dev)
+
+
 def _mask_code(causal) -> int:
     if causal is False or causal is None:
         return FA_MASK_NONE
@@ -263,12 +310,8 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
     per sequence). Returns (o [total_q,H,D], lse [H,total_q] fp32).
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
-                    ("cu_seqlens_k", cu_seqlens_k)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
+    dev = _check_inputs((("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                         ("cu_seqlens_k", cu_seqlens_k)))
     if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k, v must be 3-D [total, heads, D]")
     if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
@@ -283,10 +326,17 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, *,
         raise ValueError("q, k, v must share a dtype")
     B = cu_seqlens_q.shape[0] - 1
     if o_dtype is None:
-        o_dtype = torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float16
+        o_dtype = out.dtype if out is not None else (
+            torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float16)
+    if o_dtype not in (torch.float16, torch.bfloat16, torch.float32):
+        raise ValueError(f"o_dtype must be float16, bfloat16 or float32, not {o_dtype}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dev = q.device
+    if out is not None:
+        _check_buffer("out", out, q.shape, (o_dtype,), dev)
+    if lse is not None:
+        _check_buffer("lse", lse, (H, tq), (torch.float32,), dev)
+    _check_descales((descale_q, descale_k, descale_v), dev)
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=o_dtype, device=dev)
     if lse is None:
@@ -319,11 +369,7 @@ def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = 
     ``rng_offset`` must be the forward's.
     """
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous (BNSD)")
+    dev = _check_inputs((("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("lse", lse)))
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, S, D]")
     B, H, Sq, D = q.shape
@@ -337,10 +383,15 @@ def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = 
     if not (q.dtype == k.dtype == v.dtype == o.dtype == dout.dtype):
         raise ValueError("q, k, v, o, dout must share a dtype")
     if grad_dtype is None:
-        grad_dtype = q.dtype
+        grad_dtype = dq.dtype if dq is not None else q.dtype
+    if grad_dtype not in (q.dtype, torch.float32):
+        raise ValueError("grad_dtype must be the input dtype or float32")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dev = q.device
+    for name, t, shp in (("dq", dq, q.shape), ("dk", dk, k.shape), ("dv", dv, v.shape)):
+        if t is not None:
+            _check_buffer(name, t, shp, (grad_dtype,), dev)
+    _check_workspace(workspace, dev)
     if dq is None:
         dq = torch.empty(tuple(q.shape), dtype=grad_dtype, device=dev)
     if dk is None:
@@ -375,11 +426,7 @@ def fa_bwd(q, k, v, o, dout, lse, *, scale: float | None = None, causal: bool = 
 def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,
           out, lse, stream, num_splits, workspace, layout="BNSD", dropout=None):
     import torch
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous (BNSD)")
+    dev = _check_inputs((("q", q), ("k", k), ("v", v)))
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, S, D]")
     if layout == "BNSD":
@@ -401,10 +448,18 @@ def _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, desc
         raise ValueError("q, k, v must share a dtype")
     in_code = _dtype_code(q.dtype)
     if o_dtype is None:
-        o_dtype = torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float16
+        o_dtype = out.dtype if out is not None else (
+            torch.bfloat16 if q.dtype == torch.bfloat16 else torch.float16)
+    if o_dtype not in (torch.float16, torch.bfloat16, torch.float32):
+        raise ValueError(f"o_dtype must be float16, bfloat16 or float32, not {o_dtype}")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    dev = q.device
+    if out is not None:
+        _check_buffer("out", out, q.shape, (o_dtype,), dev)
+    if lse is not None:
+        _check_buffer("lse", lse, (B, H, Sq), (torch.float32,), dev)
+    _check_descales((descale_q, descale_k, descale_v), dev)
+    _check_workspace(workspace, dev)
     if out is None:
         out = torch.empty(tuple(q.shape), dtype=o_dtype, device=dev)
     if lse is None:

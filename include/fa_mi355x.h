@@ -65,7 +65,7 @@ typedef enum {
   FA_ERR_BAD_SHAPE = 2,            /* B, H, Sq or Sk < 1, or a size overflows 64-bit offsets or the grid */
   FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* D not in {64, 128} */
   FA_ERR_UNSUPPORTED_DTYPE = 4,    /* (in_dtype, o_dtype) pair not supported */
-  FA_ERR_UNSUPPORTED_LAYOUT = 5,   /* layout other than FA_LAYOUT_BNSD */
+  FA_ERR_UNSUPPORTED_LAYOUT = 5,   /* layout not one of fa_layout_t */
   FA_ERR_UNSUPPORTED_DROPOUT = 6,  /* keep_prob != 1.0 (dropout is not implemented) */
   FA_ERR_BAD_SCALE = 7,            /* scale is NaN or infinite */
   FA_ERR_MISALIGNED = 8,           /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
@@ -274,7 +274,10 @@ fa_status_t fa_bwd_dropout(const void* q, const void* k, const void* v, const vo
                            void* workspace, int64_t workspace_size, hipStream_t stream);
 
 /* Workspace bytes fa_bwd needs (8 bytes per query row, rows rounded up to a
- * multiple of 32 per head); -1 for sizes it rejects. */
+ * multiple of 32 per head); -1 for sizes it rejects: the kernels address
+ * the workspace with 32-bit byte offsets, so B * H * (Sq rounded up to 32)
+ * * 8 must not exceed INT32_MAX (at most 268,435,455 padded query rows over
+ * all heads), and fa_bwd returns FA_ERR_BAD_SHAPE for larger problems. */
 int64_t fa_bwd_workspace_size(int64_t B, int64_t H, int64_t Sq);
 
 /* Human-readable name of a status code ("FA_OK", ...); never NULL. */
