@@ -635,8 +635,15 @@ struct BwdDq {
   }
 };
 
+// Two waves per SIMD; the D = 128 dropout instances, whose Philox state does
+// not fit beside the 32 K fragments and the two 64-register accumulators of
+// that budget (the compiler spilled about 30 VGPRs to scratch), get one.
+template <int D, bool DROP>
+constexpr int dkv_waves_per_simd() { return (DROP && D == 128) ? 1 : 2; }
+
 template <int D, bool CAUSAL, int KIND, int OUT, bool DROP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dkv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(dkv_waves_per_simd<D, DROP>())))
+void fa_bwd_dkv_kernel(BwdParams p) {
   using Blk = BwdDkv<D, CAUSAL, KIND, OUT, DROP>;
   __shared__ __attribute__((aligned(1024))) char smem[Blk::SMEM];
   Blk blk(p, smem);

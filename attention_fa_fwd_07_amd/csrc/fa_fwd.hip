@@ -151,7 +151,7 @@ struct FwdTile {
   const Params& p;
   uint32_t lds0;                    // LDS byte address of the tile buffers
   int tid, lane, wave, hl, l32;
-  int bh, jbeg, ntiles, jlast;     // tiles jbeg .. ntiles-1 of this block (split-KV: one range)
+  int bh, ntiles, jlast;           // tiles 0 .. ntiles-1 of this block (split-KV: of its range)
   int split;
   int64_t Sq, Sk, q0, qw0, qrow;
   const char* khead;
@@ -242,14 +242,23 @@ struct FwdTile {
       if (kend < 0) kend = 0;   // every row of the block lies above the diagonal
     }
     ntiles = (int)((kend + BN - 1) / BN);
-    jbeg = 0;
     if constexpr (SPLIT) {
       // range `split` of nsplit near-equal ranges of the block's tiles
-      // (empty when there are more ranges than tiles)
+      // (empty when there are more ranges than tiles). The range becomes a
+      // problem of its own: its first key is key 0 (K and V start there,
+      // Sk and the causal offset move with it), so the loop below is the
+      // one of a whole block.
       const int per = (ntiles + p.nsplit - 1) / p.nsplit;
-      jbeg = split * per;
-      ntiles = jbeg + per < ntiles ? jbeg + per : ntiles;
-      if (jbeg > ntiles) jbeg = ntiles;
+      int jb = split * per;
+      const int je = jb + per < ntiles ? jb + per : ntiles;
+      if (jb > je) jb = je;
+      const int64_t k0 = (int64_t)jb * BN;
+      khead += k0 * kpitch;
+      vhead += k0 * kpitch;
+      const int64_t kmax = (int64_t)je * BN;
+      Sk = (kmax < Sk ? kmax : Sk) - k0;
+      moff -= k0;
+      ntiles = je - jb;
     }
     jlast = ntiles - 1;   // last tile this wave needs
     if constexpr (CAUSAL) {
@@ -649,7 +658,7 @@ struct FwdTile {
     tile<BUF>(j);
   }
 
-  // steps j+B .. j+NB-1 (tile j+b in buffer b, counting from jbeg); false
+  // steps j+B .. j+NB-1 (tile j+b in buffer b); false
   // once past the last tile
   template <int B>
   __device__ __forceinline__ bool steps_from(int j) {
@@ -664,11 +673,11 @@ struct FwdTile {
 
   __device__ __forceinline__ void run() {
     if (idle) return;   // uniform over the workgroup: no barrier is left waiting
-    // tile j lives in buffer (j - jbeg) % NB; tiles j+1 .. j+NB-1 are in flight
+    // tile j lives in buffer j % NB; tiles j+1 .. j+NB-1 are in flight
 #pragma unroll
     for (int i = 0; i < NB - 1; ++i)
-      if (jbeg + i < ntiles) load_tile(jbeg + i, i);
-    for (int j = jbeg; j < ntiles; j += NB)
+      if (i < ntiles) load_tile(i, i);
+    for (int j = 0; j < ntiles; j += NB)
       if (!steps_from<0>(j)) break;
     store();
   }

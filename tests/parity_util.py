@@ -127,7 +127,8 @@ def grad_bounds(q, k, v, g, scale, causal, off, drop=None, o_used=None, lse_used
                 E[1][b, kv] += sc * p.T @ (dd * aq)
             if lse_used is not None:
                 both_empty = np.isneginf(lse_ex) & np.isneginf(lse_used[b, h])
-                d = np.where(both_empty, 0.0, lse_ex - lse_used[b, h])
+                with np.errstate(invalid="ignore"):
+                    d = np.where(both_empty, 0.0, lse_ex - lse_used[b, h])
                 eps = np.abs(np.expm1(d))[:, None]
                 ds = np.abs(p * (dp - delta)) * eps
                 E[0][b, h] += sc * ds @ ak
