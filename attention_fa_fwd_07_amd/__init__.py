@@ -28,6 +28,7 @@ FA_ERR_ALIASING = 9
 FA_ERR_HIP = 10
 FA_ERR_WORKSPACE = 11
 FA_ERR_UNSUPPORTED_MASK = 12
+FA_ERR_SCRATCH = 13
 
 FA_LAYOUT_BNSD = 0
 FA_LAYOUT_BSHD = 1
@@ -35,6 +36,7 @@ FA_F16, FA_BF16, FA_FP8_E4M3, FA_F32 = 0, 1, 2, 3
 FA_MASK_NONE, FA_MASK_CAUSAL_TOP_LEFT, FA_MASK_CAUSAL_BOTTOM_RIGHT = 0, 1, 2
 
 EXPORTS = ("fa_fwd", "fa_fwd_ex", "fa_fwd_splitkv", "fa_fwd_splitkv_workspace_size",
+           "fa_fwd_splitkv_noalloc",
            "fa_fwd_varlen", "fa_fwd_dropout", "fa_bwd", "fa_bwd_dropout", "fa_bwd_workspace_size", "fa_status_str",
            "fa_abi_version")
 
@@ -65,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            vp]                            # stream
     lib.fa_fwd_splitkv.restype = ctypes.c_int
     lib.fa_fwd_splitkv.argtypes = lib.fa_fwd.argtypes[:-1] + [ctypes.c_int, vp, i64, vp]
+    lib.fa_fwd_splitkv_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_splitkv_noalloc.argtypes = lib.fa_fwd.argtypes[:-1] + [ctypes.c_int, vp]
     lib.fa_fwd_ex.restype = ctypes.c_int
     lib.fa_fwd_ex.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64,
                               ctypes.c_int, ctypes.c_float, ctypes.c_int, ctypes.c_float,
@@ -123,6 +127,16 @@ def fa_fwd_splitkv_raw(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, 
                                          causal, keep_prob, in_dtype, o_dtype, descale_q,
                                          descale_k, descale_v, num_splits, workspace,
                                          workspace_size, stream)
+
+
+def fa_fwd_splitkv_noalloc_raw(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale, causal, keep_prob,
+                               in_dtype, o_dtype, descale_q, descale_k, descale_v, num_splits,
+                               stream) -> int:
+    """The split-KV C entry point that allocates nothing (its workspace is a
+    static device array of the library); integer pointers, returns the status."""
+    return load_library().fa_fwd_splitkv_noalloc(q, k, v, o, lse, B, H, Sq, Sk, D, layout, scale,
+                                                 causal, keep_prob, in_dtype, o_dtype, descale_q,
+                                                 descale_k, descale_v, num_splits, stream)
 
 
 def fa_fwd_ex_raw(q, k, v, o, lse, B, H, H_kv, Sq, Sk, D, layout, scale, mask, keep_prob,

@@ -41,6 +41,7 @@
 #include <math.h>
 #include <float.h>
 #include <type_traits>
+#include <mutex>
 
 #include "fa_mi355x.h"
 
@@ -1047,6 +1048,43 @@ int64_t workspace_bytes(int64_t BH, int64_t Sq, int64_t D, int nsplit) {
 
 }  // namespace
 
+// Workspace of fa_fwd_splitkv_noalloc: a static device array, held by every
+// GPU the library runs on until the process ends. In host code `scratch` is
+// a host-side stand-in; its device address comes from hipGetSymbolAddress,
+// once per device (with that device current), and only that address is
+// handed to kernels.
+static constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, which must be the
+// device of `stream`.
+fa_status_t scratch_address(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  if (stream != nullptr) {
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return FA_ERR_HIP;
+    if (sdev != dev) return FA_ERR_SCRATCH;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+      return FA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int fa_abi_version(void) { return FA_ABI_VERSION; }
@@ -1066,6 +1104,7 @@ const char* fa_status_str(fa_status_t s) {
     case FA_ERR_HIP: return "FA_ERR_HIP";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
     case FA_ERR_UNSUPPORTED_MASK: return "FA_ERR_UNSUPPORTED_MASK";
+    case FA_ERR_SCRATCH: return "FA_ERR_SCRATCH";
   }
   return "FA_ERR_UNKNOWN";
 }
@@ -1157,6 +1196,32 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   return fa_fwd_ex(q, k, v, o, lse, B, H, H, Sq, Sk, D, layout, scale,
                    causal ? FA_MASK_CAUSAL_TOP_LEFT : FA_MASK_NONE, keep_prob, in_dtype, o_dtype,
                    descale_q, descale_k, descale_v, num_splits, workspace, workspace_size, stream);
+}
+
+fa_status_t fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                   fa_layout_t layout, float scale, int causal, float keep_prob,
+                                   fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                                   const float* descale_q, const float* descale_k,
+                                   const float* descale_v, int num_splits, hipStream_t stream) {
+  // the same checks as fa_fwd_ex, before any HIP call
+  Call c;
+  const fa_status_t st = check_call(q, k, v, o, lse, B, H, H, Sq, Sk, D, layout, scale,
+                                    causal ? FA_MASK_CAUSAL_TOP_LEFT : FA_MASK_NONE, keep_prob,
+                                    in_dtype, o_dtype, descale_q, descale_k, descale_v, c);
+  if (st != FA_OK) return st;
+  if (num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_BAD_SHAPE;
+  const int ns = num_splits ? num_splits : auto_splits(c.BH, c.nqb, Sk, c.nw);
+  const int64_t need = workspace_bytes(c.BH, Sq, D, ns);
+  if (need > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const fa_status_t s2 = scratch_address(stream, &ws);
+    if (s2 != FA_OK) return s2;
+  }
+  return fa_fwd_ex(q, k, v, o, lse, B, H, H, Sq, Sk, D, layout, scale,
+                   causal ? FA_MASK_CAUSAL_TOP_LEFT : FA_MASK_NONE, keep_prob, in_dtype, o_dtype,
+                   descale_q, descale_k, descale_v, ns, ws, need > 0 ? kScratchBytes : 0, stream);
 }
 
 fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define FA_ABI_VERSION 7
+#define FA_ABI_VERSION 8
 
 typedef enum {
   FA_OK = 0,
@@ -72,7 +72,9 @@ typedef enum {
   FA_ERR_ALIASING = 9,             /* o or lse overlaps q, k, v, or each other */
   FA_ERR_HIP = 10,                 /* a kernel launch failed */
   FA_ERR_WORKSPACE = 11,           /* split-KV: workspace NULL or smaller than needed */
-  FA_ERR_UNSUPPORTED_MASK = 12     /* fa_fwd_ex: mask not one of fa_mask_t */
+  FA_ERR_UNSUPPORTED_MASK = 12,    /* fa_fwd_ex: mask not one of fa_mask_t */
+  FA_ERR_SCRATCH = 13              /* fa_fwd_splitkv_noalloc: the problem needs more than its
+                                      static workspace, or `stream` is not on the current device */
 } fa_status_t;
 
 /* Memory layouts of q, k, v and o (contiguous): BNSD = [B, heads, S, D];
@@ -152,6 +154,27 @@ fa_status_t fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
  */
 int64_t fa_fwd_splitkv_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
                                       int causal, int num_splits);
+
+/*
+ * fa_fwd_splitkv_noalloc — fa_fwd_splitkv for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid it): it allocates nothing and takes no workspace.
+ * The partial results live in a static 64 MiB device array of the library
+ * (each GPU the library runs on holds one until the process ends), so a
+ * problem whose fa_fwd_splitkv_workspace_size(B, H, Sq, Sk, D, causal,
+ * num_splits) exceeds 67108864 bytes is rejected with FA_ERR_SCRATCH, and
+ * so is a `stream` that does not belong to the current device. Nothing in
+ * the array needs to start at zero. All calls on one GPU share its array:
+ * calls that overlap in time on one GPU (several streams, several host
+ * threads) race and give wrong results; serialise them. Other arguments,
+ * results and errors as fa_fwd_splitkv.
+ */
+fa_status_t fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t D,
+                                   fa_layout_t layout, float scale, int causal, float keep_prob,
+                                   fa_dtype_t in_dtype, fa_dtype_t o_dtype,
+                                   const float* descale_q, const float* descale_k,
+                                   const float* descale_v, int num_splits, hipStream_t stream);
 
 /*
  * fa_fwd_ex — the general entry point behind fa_fwd and fa_fwd_splitkv:

@@ -41,11 +41,11 @@ def test_library_holds_gfx950_code():
 
 def test_abi_version_and_status_strings():
     lib = fa.load_library()
-    assert lib.fa_abi_version() == 7
-    names = [fa.status_str(c) for c in range(13)]
+    assert lib.fa_abi_version() == 8
+    names = [fa.status_str(c) for c in range(14)]
     assert names[0] == "FA_OK" and names[10] == "FA_ERR_HIP" and names[11] == "FA_ERR_WORKSPACE"
-    assert names[12] == "FA_ERR_UNSUPPORTED_MASK"
-    assert len(set(names)) == 13
+    assert names[12] == "FA_ERR_UNSUPPORTED_MASK" and names[13] == "FA_ERR_SCRATCH"
+    assert len(set(names)) == 14
     assert fa.status_str(99) == "FA_ERR_UNKNOWN"
 
 
@@ -149,6 +149,38 @@ def test_splitkv_workspace_size():
 ])
 def test_splitkv_rejects_before_launch(over, code):
     assert call_split(**over) == code
+
+
+# ---- the split-KV entry point that allocates nothing ----
+def call_noalloc(**over):
+    a = dict(q=Q, k=K, v=V, o=O, lse=L, B=1, H=2, Sq=64, Sk=1024, D=128,
+             layout=fa.FA_LAYOUT_BNSD, scale=0.125, causal=0, keep_prob=1.0,
+             in_dtype=fa.FA_F16, o_dtype=fa.FA_F16, descale_q=None, descale_k=None,
+             descale_v=None, num_splits=4, stream=None)
+    a.update(over)
+    return fa.fa_fwd_splitkv_noalloc_raw(**a)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(q=None), fa.FA_ERR_NULL_POINTER),
+    (dict(D=96), fa.FA_ERR_UNSUPPORTED_HEAD_DIM),
+    (dict(num_splits=-1), fa.FA_ERR_BAD_SHAPE),
+    (dict(num_splits=257), fa.FA_ERR_BAD_SHAPE),
+    (dict(keep_prob=0.5), fa.FA_ERR_UNSUPPORTED_DROPOUT),
+    # 64 ranges of 8 * 32 * 1024 rows of 129 floats: 541 MB, over the 64 MiB array
+    (dict(B=8, H=32, Sq=1024, num_splits=64), fa.FA_ERR_SCRATCH),
+    # just over: 2 ranges of B*H*Sq rows with (D + 1) floats each
+    (dict(B=1, H=64, Sq=1017, D=128, num_splits=2), fa.FA_ERR_SCRATCH),
+])
+def test_noalloc_rejects_before_launch(over, code):
+    assert call_noalloc(**over) == code
+
+
+def test_noalloc_limit_is_the_workspace_size():
+    """The largest accepted problem is the one whose split-KV workspace fits
+    64 MiB (checked by size only: the largest that fits needs the array)."""
+    assert fa.splitkv_workspace_size(1, 64, 1017, 1024, 128, False, 2) > 64 << 20
+    assert fa.splitkv_workspace_size(1, 64, 1016, 1024, 128, False, 2) <= 64 << 20
 
 
 # ---- the general entry point ----
