@@ -101,8 +101,13 @@ __device__ __forceinline__ float unpack_hi(uint32_t x) {
 // The K swizzle spreads the 16 rows that one ds_read_b128 phase touches over
 // all 64 banks. The V swizzle for 16-bit data spreads the four rows that one
 // transposing read (ds_read_b64_tr_b16) touches over four different 64-byte
-// bank groups; fp8 V (ds_read_b64_tr_b8) uses the K pattern. Every swizzle
-// depends on the row index mod 16 only.
+// bank groups. A half-wave of fp8 V reads (ds_read_b64_tr_b8) touches eight
+// rows, {0,1,2,3,8,9,10,11} + 4*hl, two 16-byte chunks each: at a 128-byte
+// pitch the even rows share one 128-byte half of the banks and the odd rows
+// the other, so the swizzle gives the four even (odd) rows four different
+// chunk pairs (the K pattern would pair them up, a two-way conflict on every
+// V read); at a 64-byte pitch the K pattern already separates them. Every
+// swizzle depends on the row index mod 16 only.
 template <int RB>
 __device__ __forceinline__ int swz_k(int r) {
   if constexpr (RB == 256) return r & 15;
@@ -111,7 +116,8 @@ __device__ __forceinline__ int swz_k(int r) {
 }
 template <int RB, bool TR8>
 __device__ __forceinline__ int swz_v(int r) {
-  if constexpr (TR8) return swz_k<RB>(r);
+  if constexpr (TR8 && RB == 128) return (((r >> 1) & 1) | ((r >> 2) & 2)) << 1;
+  else if constexpr (TR8) return swz_k<RB>(r);
   else if constexpr (RB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
   else return ((r >> 1) & 1) << 2;
 }
