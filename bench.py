@@ -162,6 +162,30 @@ def cpu_baseline_bwd(cfg, inp, dout, budget_s: float):
             "cpu": cpu_model()}
 
 
+def gemm_ceiling(torch, steps, warmup):
+    """torch.matmul (hipBLASLt) on 8192^3 fp16 and bf16 operands: one JSON
+    line per type with the mean time per product (HIP events)."""
+    n = 8192
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    for dt in (torch.float16, torch.bfloat16):
+        a = torch.randn(n, n, device="cuda:0", generator=g).to(dt)
+        b = torch.randn(n, n, device="cuda:0", generator=g).to(dt)
+        for _ in range(warmup):
+            c = a @ b
+        torch.cuda.synchronize()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(steps):
+            c = a @ b
+        e.record()
+        torch.cuda.synchronize()
+        ms = s.elapsed_time(e) / steps
+        print(json.dumps({"gemm": f"{n}^3", "dtype": str(dt).replace("torch.", ""),
+                          "ms": round(ms, 4), "tflops": round(2 * n ** 3 / ms / 1e9, 1),
+                          "frac_of_dense_peak": round(2 * n ** 3 / ms / 1e9 / PEAK_TFLOPS["f16"], 4)}))
+        del a, b, c
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -175,6 +199,10 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a 512 MiB device-to-device copy (reference kernel "
                          "of known traffic for the HBM byte counters)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="only time the library GEMM (torch.matmul, hipBLASLt) at 8192^3 "
+                         "in fp16 and bf16: the dense MFMA rate a tuned GEMM reaches on "
+                         "this GPU, context for the attention kernel's fraction")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the attention forward here is a "
@@ -191,6 +219,9 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling(torch, args.steps, args.warmup)
         return
     import attention_fa_fwd_07_amd as fa
     import fa_inputs as fi
