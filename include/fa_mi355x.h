@@ -1,5 +1,6 @@
 /*
- * libfa_mi355x — FlashAttention forward for AMD Instinct MI355X (gfx950).
+ * libfa_mi355x — FlashAttention forward (and its backward) for AMD Instinct
+ * MI355X (gfx950).
  *
  * C ABI. Plain pointers and sizes; no C++ or framework types cross it.
  *
@@ -44,8 +45,10 @@
  * error other than FA_ERR_HIP nothing is launched and the outputs are
  * untouched.
  *
- * Thread safety: fa_fwd keeps no mutable state and may be called from
- * several threads on different streams.
+ * Thread safety: the entry points keep no mutable state (except the
+ * per-device address cache of fa_fwd_splitkv_noalloc, taken under a lock)
+ * and may be called from several threads on different streams; calls of
+ * fa_fwd_splitkv_noalloc that overlap on one GPU race on its array.
  */
 #ifndef FA_MI355X_H
 #define FA_MI355X_H
@@ -66,7 +69,8 @@ typedef enum {
   FA_ERR_UNSUPPORTED_HEAD_DIM = 3, /* D not in {64, 128} */
   FA_ERR_UNSUPPORTED_DTYPE = 4,    /* (in_dtype, o_dtype) pair not supported */
   FA_ERR_UNSUPPORTED_LAYOUT = 5,   /* layout not one of fa_layout_t */
-  FA_ERR_UNSUPPORTED_DROPOUT = 6,  /* keep_prob != 1.0 (dropout is not implemented) */
+  FA_ERR_UNSUPPORTED_DROPOUT = 6,  /* keep_prob != 1.0 on an entry point without dropout, or
+                                      keep_prob outside (0, 1] for fa_fwd_dropout / fa_bwd_dropout */
   FA_ERR_BAD_SCALE = 7,            /* scale is NaN or infinite */
   FA_ERR_MISALIGNED = 8,           /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   FA_ERR_ALIASING = 9,             /* o or lse overlaps q, k, v, or each other */
