@@ -303,7 +303,8 @@ def fa_fwd_splitkv(q, k, v, *, num_splits: int = 0, scale: float | None = None,
                    descale_k=None, descale_v=None, out=None, lse=None, workspace=None,
                    stream=None, layout: str = "BNSD"):
     """fa_fwd with the keys of each query block split into ``num_splits``
-    ranges (0: chosen to fill the GPU), merged by logsumexp. ``workspace``:
+    ranges (0: chosen by the library, 1 unless the plain grid would leave
+    most of the GPU idle), merged by logsumexp. ``workspace``:
     an optional uint8 GPU tensor of at least ``splitkv_workspace_size(...)``
     bytes (allocated here when not given)."""
     return _call(q, k, v, scale, causal, keep_prob, o_dtype, descale_q, descale_k, descale_v,

@@ -1025,16 +1025,21 @@ MergeFn pick_merge(const Call& c) {
 
 constexpr int kMaxSplits = 256;
 
-// Key ranges per query block when the caller passes num_splits = 0: enough
-// workgroups for about two rounds of the 256 CUs (three 4-wave workgroups,
-// or one 8-wave workgroup, resident per CU), each range at least four
-// 32-key tiles long.
+// Key ranges per query block when the caller passes num_splits = 0. A split
+// pays for its fp32 partial results, the merge and a second launch only
+// where the plain grid leaves most of the GPU idle: blocks for fewer than
+// half the resident slots (three 4-wave workgroups per CU) and key ranges
+// of at least 16 32-key tiles. Then it aims at one full round of the slots.
+// Measured on fp16 D = 128: B1 H4 S8192 (256 blocks) 200 -> 158 us at 3
+// ranges, causal 172 -> 114; B2 H2 S4096 (128 blocks) 95 -> 59 at 6; B1 H1
+// S32768 641 -> 540 at 3; with 512 blocks (B1 H16 S4096, B2 H16 S2048
+// causal) every split was slower than the plain kernel.
 int auto_splits(int64_t BH, int64_t nqb, int64_t Sk, int nw) {
   const int64_t resident = 256 * (nw == 4 ? 3 : 1);
   const int64_t base = BH * nqb;
-  if (base >= 2 * resident) return 1;
-  int64_t s = (2 * resident + base - 1) / base;
-  const int64_t by_tiles = ((Sk + 31) / 32) / 4;
+  if (2 * base > resident) return 1;
+  int64_t s = (resident + base - 1) / base;
+  const int64_t by_tiles = ((Sk + 31) / 32) / 16;
   if (s > by_tiles) s = by_tiles;
   if (s > 64) s = 64;
   return s < 1 ? 1 : (int)s;

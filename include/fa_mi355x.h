@@ -130,9 +130,12 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
  * split partitions the same way. Results equal fa_fwd's up to rounding.
  *
  * Arguments as fa_fwd, plus:
- * num_splits: ranges per block of query rows, 0..256; 0 chooses a count
- *   that fills the GPU (1 when the plain grid already does). Ranges past the
- *   last key are empty and cost one workgroup each.
+ * num_splits: ranges per block of query rows, 0..256; 0 chooses the count:
+ *   more than one only when the blocks of query rows would fill fewer than
+ *   half of the GPU's resident workgroup slots and every range keeps at
+ *   least 16 tiles of 32 keys (then about one full round of the slots), 1
+ *   otherwise. Ranges past the last key are empty and cost one workgroup
+ *   each.
  * workspace, workspace_size: device memory of at least
  *   fa_fwd_splitkv_workspace_size(...) bytes, 256-byte aligned, owned by the
  *   caller, not overlapping any other argument; its contents on entry do not

@@ -128,7 +128,12 @@ def test_splitkv_workspace_size():
     assert fa.splitkv_workspace_size(1, 2, 64, 1024, 128, False, 1) == 0
     # automatic count: a shape that fills the GPU needs no workspace
     assert fa.splitkv_workspace_size(4, 32, 4096, 4096, 128, False, 0) == 0
-    assert fa.splitkv_workspace_size(1, 8, 512, 512, 64, False, 0) > 0
+    # the automatic count splits only grids that leave most of the GPU idle,
+    # with long key ranges
+    assert fa.splitkv_workspace_size(1, 4, 8192, 8192, 128, False, 0) == \
+        fa.splitkv_workspace_size(1, 4, 8192, 8192, 128, False, 3)
+    assert fa.splitkv_workspace_size(1, 8, 512, 512, 64, False, 0) == 0
+    assert fa.splitkv_workspace_size(1, 16, 4096, 4096, 128, True, 0) == 0
     for bad in (dict(D=96), dict(num_splits=-1), dict(num_splits=257), dict(B=0)):
         a = dict(B=1, H=2, Sq=64, Sk=1024, D=128, causal=False, num_splits=4)
         a.update(bad)
