@@ -60,13 +60,13 @@ def device_info():
     return info
 
 
-def measured_traffic():
+def measured_traffic(workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary,
-    valid only for the kernel source it was measured on."""
+    valid only for the workload and the kernel source it was measured on."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     d = json.load(open(TRAFFIC_FILE))
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("workload") != workload or d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return d.get("bytes_per_launch")
 
@@ -292,7 +292,7 @@ def main():
     achieved = flops / (avg_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": None if (bwd or args.keep_prob != 1.0) else measured_traffic(),
+                "traffic": None if (bwd or args.keep_prob != 1.0) else measured_traffic(cfg.name),
                 "kernel": "fa_bwd (row pass, dK/dV and dQ kernels; one call)" if bwd
                 else "fa_fwd_kernel", "avg_launch_ms": round(avg_ms, 4),
                 "median_launch_ms": round(med_ms, 4), "min_launch_ms": round(min(per_launch_ms), 4)}

@@ -47,8 +47,12 @@ def test_traffic_record_belongs_to_the_headline_kernel():
     assert d["bytes_per_launch"] == d["fetch_bytes"] + d["write_bytes"]
     assert abs(d["fetch_bytes"] - d["fetch_size_kib_raw"] * 1024 * d["copy_factor_fetch"]) < 1e6
     assert abs(d["write_bytes"] - d["write_size_kib_raw"] * 1024 * d["copy_factor_write"]) < 1e6
-    got = bench.measured_traffic()
+    got = bench.measured_traffic(fi.HEADLINE.name)
     if d["kernel_source_sha256_16"] == bench.kernel_source_hash():
         assert got == d["bytes_per_launch"]
     else:
         assert got is None
+    # another workload's line carries no traffic figure (it was not measured)
+    for cfg in fi.CONFIGS:
+        if cfg.name != fi.HEADLINE.name:
+            assert bench.measured_traffic(cfg.name) is None
