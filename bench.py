@@ -31,7 +31,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8_e4m3": 5033.2}   # dense MFMA, MI355X
 HBM_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_b4h32s4096d128_f16_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fa_fwd_traffic.json")
 KERNEL_SRCS = [os.path.join(ROOT, "attention_fa_fwd_07_amd", "csrc", f)
                for f in ("fa_fwd.hip", "fa_device.h")]
 
@@ -61,14 +61,16 @@ def device_info():
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    valid only for the workload and the kernel source it was measured on."""
+    """HBM bytes per launch of the forward kernel on this workload, from the
+    committed rocprofv3 counter summary (one record per workload), valid only
+    for the kernel source it was measured on."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     d = json.load(open(TRAFFIC_FILE))
-    if d.get("workload") != workload or d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get("bytes_per_launch")
+    rec = d.get("workloads", {}).get(workload)
+    return None if rec is None else rec.get("bytes_per_launch")
 
 
 def cpu_model() -> str:

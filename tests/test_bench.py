@@ -37,22 +37,22 @@ def test_cpu_baseline_of_the_backward():
     assert r["value"] > 0 and r["sample"].startswith("backward of 2 of 2 heads")
 
 
-def test_traffic_record_belongs_to_the_headline_kernel():
-    """The committed HBM-byte record names the headline kernel and workload;
-    bench.py reports its bytes only while the kernel sources still hash to
-    the recorded value (else null), and the record's bytes are the copy-
-    calibrated counter readings."""
+def test_traffic_records():
+    """The committed HBM-byte records: one per workload, each the copy-
+    calibrated counter readings; bench.py reports a workload's bytes only
+    while the kernel sources still hash to the recorded value (else null)."""
     d = json.load(open(bench.TRAFFIC_FILE))
-    assert d["workload"] == fi.HEADLINE.name
-    assert d["bytes_per_launch"] == d["fetch_bytes"] + d["write_bytes"]
-    assert abs(d["fetch_bytes"] - d["fetch_size_kib_raw"] * 1024 * d["copy_factor_fetch"]) < 1e6
-    assert abs(d["write_bytes"] - d["write_size_kib_raw"] * 1024 * d["copy_factor_write"]) < 1e6
-    got = bench.measured_traffic(fi.HEADLINE.name)
-    if d["kernel_source_sha256_16"] == bench.kernel_source_hash():
-        assert got == d["bytes_per_launch"]
-    else:
-        assert got is None
-    # another workload's line carries no traffic figure (it was not measured)
-    for cfg in fi.CONFIGS:
-        if cfg.name != fi.HEADLINE.name:
-            assert bench.measured_traffic(cfg.name) is None
+    recs = d["workloads"]
+    assert set(recs) == {c.name for c in fi.CONFIGS}
+    for name, r in recs.items():
+        assert r["bytes_per_launch"] == r["fetch_bytes"] + r["write_bytes"]
+        assert abs(r["fetch_bytes"] - r["fetch_size_kib_raw"] * 1024 * d["copy_factor_fetch"]) < 1e6
+        assert abs(r["write_bytes"] - r["write_size_kib_raw"] * 1024 * d["copy_factor_write"]) < 1e6
+        # no kernel moves fewer bytes than Q, K, V once and O, lse once
+        assert r["bytes_per_launch"] >= 0.99 * r["algorithmic_bytes"]
+        got = bench.measured_traffic(name)
+        if d["kernel_source_sha256_16"] == bench.kernel_source_hash():
+            assert got == r["bytes_per_launch"]
+        else:
+            assert got is None
+    assert bench.measured_traffic("no such workload") is None
