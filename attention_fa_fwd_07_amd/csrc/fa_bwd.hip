@@ -242,6 +242,16 @@ struct BwdDkv {
   int qt0, nqt, ntot;                         // query tiles qt0 .. nqt-1 per head
   u32x4 kf[NDS];
   f32x16 acc_k[NDB], acc_v[NDB];
+  // this lane's fragment addresses in tile buffer 0 (the buffer, the dO tile
+  // and the 16-row step are compile-time offsets added to them, so they fold
+  // into the read instructions): Q rows, V rows of this wave's keys,
+  // transposed Q (and dO) fragments, lse2/Delta. The causal instances (more
+  // live state) keep one Q row base, one V row base and one transposed-read
+  // base per row half and form each fragment's address with an XOR in the loop.
+  static constexpr int NQA = CAUSAL ? 1 : NDS;
+  static constexpr int NVA = CAUSAL ? 1 : NDS;
+  static constexpr int NTA = CAUSAL ? 1 : NDB;
+  uint32_t qa[NQA], va[NVA], ta[NTA][2], la;
 
   __device__ __forceinline__ BwdDkv(const BwdParams& p_, char* smem) : p(p_) {
     lds0 = (uint32_t)(uintptr_t)LDS_PTR(char, smem);
@@ -276,6 +286,18 @@ struct BwdDkv {
       acc_k[db] = (f32x16){};
       acc_v[db] = (f32x16){};
     }
+    const uint32_t qb0 = lds0 + ROFF;
+    const uint32_t vb = lds0 + VOFF + 32 * wave * RB;
+#pragma unroll
+    for (int ds = 0; ds < NDS; ++ds) {
+      if (ds < NQA) qa[ds] = qb0 + l32 * RB + (((2 * ds + hl) ^ swz<RB, 1>(l32)) << 4);
+      if (ds < NVA) va[ds] = vb + l32 * RB + (((2 * ds + hl) ^ swz<RB, 0>(l32)) << 4);
+    }
+#pragma unroll
+    for (int db = 0; db < NTA; ++db)
+#pragma unroll
+      for (int e = 0; e < 2; ++e) ta[db][e] = tr_addr<RB, 1>(qb0, lane, hl, db, e);
+    la = qb0 + 2 * TQ + 4 * hl * 4;
   }
 
   __device__ __forceinline__ const char* kvbase(const char* t, int64_t ss) const {
@@ -316,17 +338,65 @@ struct BwdDkv {
         if (p.negate) kf[ds] ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       }
     }
-    for (int it = 0; it < ntot; ++it) {
-      wait_loads<0>();
-      lds_barrier();
-      if (it + 1 < ntot) load_tile(it + 1, (it + 1) & 1);
-      tile(it, it & 1);
+    for (int it = 0; it < ntot; it += 2) {
+      step<0>(it);
+      if (it + 1 < ntot) step<1>(it + 1);
     }
     wait_loads<0>();   // no copy into LDS may outlive the workgroup (ntot = 0)
     store();
   }
 
-  __device__ __forceinline__ void tile(int it, int buf) {
+  // LDS addresses of this lane's Q and V row fragments of k-step ds. The
+  // chunk index is (2*ds + hl) ^ swz(row), and the row base (1 KiB-aligned
+  // block, whole rows) has zero chunk bits, so the address of k-step ds is
+  // that of k-step 0 with ds XORed into bits 5 and up; the causal instances
+  // form it in the loop (an XOR opaque to the compiler, so that it is not
+  // hoisted into a register per k-step) to stay within the register budget.
+  // ds (and db below) are unrolled loop indices: compile-time immediates.
+  __device__ __forceinline__ uint32_t q_addr(int ds) const {
+    if constexpr (NQA == NDS) {
+      return qa[ds];
+    } else {
+      uint32_t a;
+      asm volatile("v_xor_b32 %0, %2, %1" : "=v"(a) : "v"(qa[0]), "n"(ds << 5));
+      return a;
+    }
+  }
+  __device__ __forceinline__ uint32_t v_addr(int ds) const {
+    if constexpr (NVA == NDS) {
+      return va[ds];
+    } else {
+      uint32_t a;
+      asm volatile("v_xor_b32 %0, %2, %1" : "=v"(a) : "v"(va[0]), "n"(ds << 5));
+      return a;
+    }
+  }
+  // the same for the transposed reads of head-dim block db (tr_addr): the
+  // block enters the chunk index as 4*db, above the two chunk bits that the
+  // lane picks, so it is db XORed into address bits 6 and up
+  __device__ __forceinline__ uint32_t t_addr(int db, int e) const {
+    if constexpr (NTA == NDB) {
+      return ta[db][e];
+    } else {
+      uint32_t a;
+      asm volatile("v_xor_b32 %0, %2, %1" : "=v"(a) : "v"(ta[0][e]), "n"(db << 6));
+      return a;
+    }
+  }
+
+  // query tile `it` in buffer B (= it % 2, a compile-time value so that the
+  // LDS offsets fold into the instructions)
+  template <int B>
+  __device__ __forceinline__ void step(int it) {
+    wait_loads<0>();
+    lds_barrier();
+    if (it + 1 < ntot) load_tile(it + 1, B ^ 1);
+    tile<B>(it);
+  }
+
+  template <int B>
+  __device__ __forceinline__ void tile(int it) {
+    constexpr uint32_t off = B * BUF;
     const int per = nqt - qt0;
     const int hh = it / per;
     const int64_t q0 = (int64_t)(qt0 + (it - hh * per)) * BQ;
@@ -334,10 +404,6 @@ struct BwdDkv {
       // every key of this wave lies above the diagonal for all 32 rows
       if (kw0 > q0 + BQ - 1 + p.moff) return;
     }
-    const uint32_t qb = lds0 + ROFF + buf * BUF;
-    const uint32_t ob = qb + TQ;
-    const uint32_t lb = qb + 2 * TQ;
-    const uint32_t vb = lds0 + VOFF + 32 * wave * RB;
     uint32_t zbits = 0;   // dropout: bit r = keep bit of this lane's key in row r
     if constexpr (DROP) {
       // this lane draws row q0 + l32, half hl of the wave's 32-key tile and
@@ -361,10 +427,10 @@ struct BwdDkv {
     // S = Q K^T, dP = dO V^T: lane = key (l32), rows = queries
     f32x16 s = (f32x16){}, dp = (f32x16){};
 #pragma unroll
-    for (int ds = 0; ds < NDS; ++ds) s = mfma32<KIND>(row_frag<RB, 1>(qb, l32, ds, hl), kf[ds], s);
+    for (int ds = 0; ds < NDS; ++ds) s = mfma32<KIND>(lds_load<u32x4>(q_addr(ds) + off), kf[ds], s);
 #pragma unroll
     for (int ds = 0; ds < NDS; ++ds)
-      dp = mfma32<KIND>(row_frag<RB, 1>(ob, l32, ds, hl), row_frag<RB, 0>(vb, l32, ds, hl), dp);
+      dp = mfma32<KIND>(lds_load<u32x4>(q_addr(ds) + off + TQ), lds_load<u32x4>(v_addr(ds)), dp);
 
     // P = exp2(S*c - lse2), dS = P * (dP - Delta); register r holds query
     // row 8*(r/4) + 4*hl + r%4 of the tile
@@ -378,8 +444,8 @@ struct BwdDkv {
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 l2 = lds_load<f32x4>(lb + (8 * g + 4 * hl) * 4);
-      const f32x4 dl = lds_load<f32x4>(lb + 128 + (8 * g + 4 * hl) * 4);
+      const f32x4 l2 = lds_load<f32x4>(la + off + 8 * g * 4);
+      const f32x4 dl = lds_load<f32x4>(la + off + 128 + 8 * g * 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * g + e;
@@ -407,11 +473,12 @@ struct BwdDkv {
     for (int st = 0; st < 2; ++st) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
-        const uint32_t so = st * 16 * RB;
-        const u32x4 a = tr_frag(tr_addr<RB, 1>(ob + so, lane, hl, db, 0), tr_addr<RB, 1>(ob + so, lane, hl, db, 1));
+        const uint32_t so = off + st * 16 * RB;
+        const uint32_t t0 = t_addr(db, 0), t1 = t_addr(db, 1);
+        const u32x4 a = tr_frag(t0 + so + TQ, t1 + so + TQ);
         acc_v[db] = mfma32<KIND>(a, pf[st], acc_v[db]);
-        const u32x4 qa = tr_frag(tr_addr<RB, 1>(qb + so, lane, hl, db, 0), tr_addr<RB, 1>(qb + so, lane, hl, db, 1));
-        acc_k[db] = mfma32<KIND>(qa, dsf[st], acc_k[db]);
+        const u32x4 qt = tr_frag(t0 + so, t1 + so);
+        acc_k[db] = mfma32<KIND>(qt, dsf[st], acc_k[db]);
       }
     }
   }
