@@ -197,11 +197,11 @@ fa_status_t fa_fwd_splitkv_noalloc(const void* q, const void* k, const void* v, 
  *   comes from fa_fwd_splitkv_workspace_size(B, H, Sq, Sk, D, mask != 0,
  *   num_splits).
  * Other arguments, ownership and errors as fa_fwd; H_kv < 1, H_kv > H or
- * H % H_kv != 0 is FA_ERR_BAD_SHAPE. The variants come from the survey of
- * the pages' call (the npu_flash_attention call has head_num and a layout;
- * grouped heads and the bottom-right diagonal are the pages' Sq != Sk and
- * layout-contract lessons, "Hygon FlashAttention: fixed-defect review",
- * item 12).
+ * H % H_kv != 0 is FA_ERR_BAD_SHAPE. The variants follow the pages' call
+ * and lessons: the npu_flash_attention call takes head_num and a layout;
+ * grouped heads and the bottom-right diagonal are the Sq != Sk and
+ * layout-contract lessons of "Hygon FlashAttention: fixed-defect review",
+ * item 12.
  */
 fa_status_t fa_fwd_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                       int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t D,
