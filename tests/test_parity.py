@@ -60,7 +60,26 @@ def _heads_to_check(cfg, rng):
 
 @pytest.mark.parametrize("idx", range(len(fi.CONFIGS)), ids=[c.name for c in fi.CONFIGS])
 def test_workload_full_size(idx):
-    cfg = fi.CONFIGS[idx]
+    _check_large(fi.CONFIGS[idx], idx)
+
+
+# 16-bit D = 64 grids of at least 2048 workgroups run with four workgroups per
+# CU (the library sizes their LDS for that), smaller ones with three; these
+# cover the larger setting, the workloads above the smaller one.
+D64_LARGE = [fi.Config("b2h32s4096d64_f16", 2, 32, 4096, 4096, 64, fi.F16, False, seed=611, scale=0.125),
+             fi.Config("b4h16s4096d64_bf16_causal", 4, 16, 4096, 4096, 64, fi.BF16, True, seed=612,
+                       o_dtype=fi.BF16, scale=0.125),
+             fi.Config("b1h64s4100d64_f16_causal", 1, 64, 4100, 4100, 64, fi.F16, True, seed=613, scale=0.125)]
+
+
+@pytest.mark.parametrize("k", range(len(D64_LARGE)), ids=[c.name for c in D64_LARGE])
+def test_d64_four_per_cu(k):
+    cfg = D64_LARGE[k]
+    assert cfg.B * cfg.H * ((cfg.Sq + 127) // 128) >= 2048
+    _check_large(cfg, 100 + k)
+
+
+def _check_large(cfg, idx):
     inp = fi.make_inputs(cfg)
     rng = np.random.default_rng(idx)
     whole, sampled = _heads_to_check(cfg, rng)
