@@ -794,11 +794,15 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
   if (d == 0) p.lse[row] = sum > 0.f ? m + logf(sum) : -INFINITY;
 }
 
-// 32-key tiles in a ring of FA_NBUF buffers per tensor: 2 x 3 x 32 x D x 2
-// bytes (48 KiB at D = 128). At least three waves per SIMD, so the register
-// budget is capped at a third of the file.
+// Tiles in a ring of FA_NBUF buffers per tensor: two, 2 x 2 x 32 x D x 2
+// bytes (32 KiB) for 32-key 16-bit tiles at D = 128. The loads of tile j+1
+// then have the compute of tile j to arrive, which covers them: against a
+// ring of three (48 KiB) two measured 0.2-0.7 % faster on every D = 128
+// workload and 1.4 % on the dropout forward, same outputs bit for bit
+// (deeper rings gave nothing either). At least three waves per SIMD, so the
+// register budget is capped at a third of the file.
 #ifndef FA_NBUF
-#define FA_NBUF 3
+#define FA_NBUF 2
 #endif
 // Waves per workgroup (32 query rows each): four, i.e. three workgroups per
 // CU. (Causal D = 64 ran faster with 8-wave workgroups while each XCD took
@@ -807,13 +811,14 @@ __global__ __launch_bounds__(256) void fa_merge_kernel(MergeParams p) {
 // keeps any power-of-two wave count.)
 __host__ __device__ constexpr int waves_for(int d, bool causal) { return 4; }
 // Keys per tile: 64 where a K/V row is 128 bytes (fp8 at D=128, anything at
-// D=64: the ring of three still leaves room for three workgroups per CU;
+// D=64: the ring still leaves room for three workgroups per CU;
 // measured 7.5 % faster on B1 H32 S8192 D128 fp8 causal, 8.5 % on B3 H12
 // S4097 D64 causal, 17 % on B1 H8 S512 D64), 32 for 16-bit data at D=128
 // (64 would leave one workgroup per CU).
 __host__ __device__ constexpr int keys_for(int kind, int d) { return (kind == KFP8 || d == 64) ? 64 : 32; }
-// 16-bit data at D = 64 (a 64-key tile is 8 KiB per tensor): a ring of two
-// buffers (32 KiB) and at most 128 VGPRs, so four workgroups can share a CU.
+// 16-bit data at D = 64 (a 64-key tile is 8 KiB per tensor): always a ring
+// of two buffers (32 KiB) and at most 128 VGPRs, so four workgroups can
+// share a CU.
 // Its LDS is dynamic and the host sizes it per launch: 32 KiB (four
 // workgroups per CU) for grids of at least DYN_LDS_MIN_GRID workgroups, else
 // 48 KiB, which keeps three per CU. Measured against the ring of three at
