@@ -23,9 +23,10 @@
 //    product in registers (no LDS round trip), with the key order inside a
 //    16-key step chosen to match the accumulator layout.
 //  * K and V tiles go from HBM straight into LDS (global_load_lds, 16 bytes
-//    per lane), through a ring of three buffers (two tiles in flight while
-//    one is computed on), in an XOR-swizzled layout chosen per head dim; K is read with ds_read_b128, V with the transposing
-//    ds_read_b64_tr_b16, which delivers V^T fragments directly.
+//    per lane), through a ring of two buffers (the next tile in flight while
+//    one is computed on), in an XOR-swizzled layout chosen per head dim; K
+//    is read with ds_read_b128, V with the transposing ds_read_b64_tr_b16,
+//    which delivers V^T fragments directly.
 //  * Tail guards: rows past Sq or Sk are clamped to the last valid row, so
 //    every load reads mapped memory holding finite values; keys past Sk and
 //    keys above the causal diagonal are set to -inf before the softmax, and
